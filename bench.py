@@ -1,0 +1,207 @@
+"""Decoder-block prefill throughput of libblock on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward pass of the whole block (every kernel of the path)
+over one batch of seeded synthetic input already resident in HBM.  The
+default workload is the Llama-7B-shape block (batch 4 x seq 2048, hidden
+4096, 32/32 heads of 128, SwiGLU width 10928, bf16 operands, float32
+accumulation).  Prints one JSON line.
+
+Per-kernel times come from HIP events that libblock records on its own
+stream inside the timed steps (blk_profile_begin/end); the roofline object
+reports the dominant kernel's algorithmic FLOP rate against the bf16 dense
+MFMA peak.  cpu_baseline times the fp64 CPU oracle on a bounded sample of
+the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block prefill tokens/s at Llama-7B shape bf16, 1 MI355X; % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_pairs(w, mask):
+    """Number of (query, key) pairs attention must evaluate: causal, inside
+    the window, key not padded; summed over the batch (per head)."""
+    import numpy as np
+    tot = 0
+    for b in range(w.B):
+        real = np.ones(w.S, bool) if mask is None else mask[b] != 0
+        for i in range(w.S):
+            lo = 0 if w.window <= 0 else max(0, i - w.window + 1)
+            tot += int(real[lo:i + 1].sum()) if mask is not None else (i - lo + 1)
+    return tot
+
+
+def kernel_work(w, mask):
+    """Algorithmic FLOPs (MFMA kernels) or HBM bytes (row kernels) of one
+    launch of each kernel of the block, by profile name."""
+    T, H, nh, nkv, hd = w.T, w.H, w.nh, w.nkv, w.hd
+    es = 2 if w.dtype == "bf16" else 4
+    f = {}
+    f["gemm_qkv"] = ("flop", 2.0 * T * H * ((nh + 2 * nkv) * hd + w.head_gate))
+    f["attention"] = ("flop", 4.0 * hd * nh * visible_pairs(w, mask))
+    f["gemm_o"] = ("flop", 2.0 * T * nh * hd * H)
+    if w.mlp == "swiglu":
+        f["gemm_up"] = ("flop", 2.0 * T * H * 2 * w.I)
+        f["gemm_down"] = ("flop", 2.0 * T * w.I * H)
+    elif w.mlp in ("relu2", "xielu"):
+        f["gemm_up"] = ("flop", 2.0 * T * H * w.I)
+        f["gemm_down"] = ("flop", 2.0 * T * w.I * H)
+    else:
+        k = w.top_k
+        f["gemm_router"] = ("flop", 2.0 * T * H * w.E)
+        f["gemm_expert_up"] = ("flop", 2.0 * T * k * H * 2 * w.I_e)
+        f["gemm_expert_down"] = ("flop", 2.0 * T * k * w.I_e * H)
+        if w.n_shared:
+            f["gemm_shared_up"] = ("flop", 2.0 * T * H * 2 * w.I_sh)
+            f["gemm_shared_down"] = ("flop", 2.0 * T * w.I_sh * H)
+        f["combine"] = ("byte", T * H * (k * es + 4 + 4 + es) + H * es)
+        f["topk"] = ("byte", T * w.E * es + T * k * 8)
+    f["rmsnorm_in"] = ("byte", 2.0 * T * H * es + H * es)
+    f["rmsnorm_mlp"] = ("byte", T * H * (4 + es) + H * es)
+    f["norm_add_norm"] = ("byte", T * H * (4 + es + 4 + es) + 2 * H * es)
+    f["post_mlp_norm"] = ("byte", T * H * (4 + 4 + es) + H * es)
+    return f
+
+
+def total_flops(work):
+    return sum(v for kind, v in work.values() if kind == "flop")
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The fp64 oracle on a bounded sample: the first R tokens of sequence 0
+    of the same workload (all of them computed, attention over their causal
+    prefix), R grown until the run takes a few seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import block as ob
+    from transformer_decoder_block_amd import synth
+    R = 64
+    cfg = w.as_dict()
+    best = None
+    while True:
+        w2 = w.replace(B=1, S=R, pad=0)
+        W = synth.weights_f64(w2, synth.make_weights(w2))
+        x = synth.to_f64(synth.make_x(w2), w.dtype)
+        t0 = time.perf_counter()
+        ob.block_forward(x[0], None, W, cfg)
+        dt = time.perf_counter() - t0
+        best = (R, dt)
+        if dt > budget_s / 4 or R >= w.S or R >= 2048:
+            break
+        R = min(w.S, R * 4)
+    R, dt = best
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": R / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {R} tokens of sequence 0 ({w.name} shapes and weights), "
+                      f"fp64 NumPy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs the block on one GPU; "
+                          "--gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from transformer_decoder_block_amd import binding as L
+    from transformer_decoder_block_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    Wst = synth.make_weights(w)
+    xst = synth.make_x(w)
+    mask = synth.make_mask(w)
+
+    def dev(a):
+        if isinstance(a, float):
+            return a
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    Wd = {k: dev(v) for k, v in Wst.items()}
+    x = dev(xst)
+    maskd = None if mask is None else torch.from_numpy(mask).cuda()
+    y = torch.empty_like(x)
+    blk = L.Block(L.make_config(w), Wd)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            blk.forward(x, y, maskd, stream=stream)
+    torch.cuda.synchronize()
+
+    # timed region: K steps on one stream, per-kernel events recorded inside
+    L.blk_profile_begin(blk.h, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.forward(x, y, maskd, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = L.blk_profile_end(blk.h) or []
+    ms_step = wall * 1e3 / args.steps
+
+    work = kernel_work(w, mask)
+    flops = total_flops(work)
+    per_kernel = {}
+    for name, tot_ms, calls in prof:
+        avg = tot_ms / max(1, calls)
+        ent = {"ms": round(avg, 4)}
+        if name in work:
+            kind, amount = work[name]
+            if kind == "flop":
+                ent["tflops"] = round(amount / (avg * 1e-3) / 1e12, 1)
+            else:
+                ent["gbs"] = round(amount / (avg * 1e-3) / 1e9, 1)
+        per_kernel[name] = ent
+    flop_kernels = [(n, e) for n, e in per_kernel.items() if "tflops" in e]
+    dom_name, dom = max(flop_kernels, key=lambda t: t[1]["ms"])
+    peak = PEAK_TFLOPS[w.dtype]
+    roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak,
+            "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4),
+            "traffic": None, "kernel": dom_name,
+            "flop_per_launch": work[dom_name][1]}
+    tokens = w.T
+    value = tokens / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "seq": w.S, "hidden": w.H,
+                   "heads": w.nh, "kv_heads": w.nkv, "head_dim": w.hd,
+                   "mlp": w.mlp, "intermediate": w.I or w.I_e,
+                   "parallelism": "none (1 GPU)"},
+        "block_tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
+        "block_frac_of_peak": round(flops / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "gflop_per_step": round(flops / 1e9, 1),
+        "roofline": roof,
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

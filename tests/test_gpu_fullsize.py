@@ -1,0 +1,98 @@
+"""GPU parity at the full sizes of the four bf16 workloads, in the launch
+configuration bench.py times (one handle created for the workload's own
+batch and sequence).
+
+The oracle evaluates sampled query rows one by one (their causal or window
+prefix of keys is projected in full), chosen to cover the first and last
+tokens, tile edges, the window edge and the padded tail; bars and the
+stagewise protocol are those of test_gpu_parity.py.  Integer work is
+checked on every token: the router's choice over all T tokens equals the
+oracle's choice from the same logits, and y equals the bf16 rounding of
+the float32 layer_output everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import block as ob
+from transformer_decoder_block_amd import synth
+from tests import bf16_emulation as em
+from tests.blockrun import Run, host, rel_err
+from tests.test_gpu_parity import BF16_BAR, check_scores, floor_bar
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["llama7b_bf16", "arcee_gqa_bf16", "apertus_bf16", "afmoe_bf16"]
+
+
+def sample_rows(w):
+    S = w.S
+    rows = {0, 1, 31, 32, 63, 64, 127, 128, 129, S // 2, S - 2, S - 1,
+            min(S - 1, 4095)}
+    if w.window:
+        rows |= {w.window - 1, w.window, w.window + 1, 2 * w.window + 5}
+    if w.pad:
+        rows |= {S - w.pad - 1, S - w.pad, S - w.pad + 1}
+    rng = np.random.default_rng(1234)
+    rows |= set(rng.integers(0, S, 8).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < S))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_stagewise(name):
+    w = synth.WORKLOADS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    run = Run(w)
+    taps = ["attention_norm_output", "layer_mid", "mlp_input", "layer_output"]
+    if w.mlp == "moe":
+        taps += ["router_logits", "expert_indices", "expert_weights"]
+    if name == "llama7b_bf16":
+        taps += ["attention_scores"]
+    print(f"[fullsize] {name}: forward", flush=True)
+    d = run.forward(taps, on_device=True)
+    # y is the bf16 rounding of the float32 layer_output, on every element
+    assert torch.equal(d["layer_output"].to(torch.bfloat16).view(torch.int16),
+                       d["y_raw"].view(torch.int16))
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    rows = sample_rows(w)
+    if w.mlp == "moe":
+        # the router's choice over every token, from the GPU's own logits
+        lg = host(d["router_logits"]).reshape(-1, w.E)
+        _, idx, wts = ob.route(lg, W["expert_bias"], w.top_k, w.route_scale, "bf16")
+        assert np.array_equal(d["expert_indices"].cpu().numpy().reshape(-1, w.top_k), idx)
+        np.testing.assert_allclose(host(d["expert_weights"]).reshape(-1, w.top_k), wts,
+                                   rtol=2e-6, atol=1e-7)
+    for b in sorted({0, w.B - 1}):
+        print(f"[fullsize] {name}: oracle, sequence {b}", flush=True)
+        mk = None if run.mask is None else run.mask[b]
+        a_tap = host(d["attention_norm_output"][b])
+        mid_tap = host(d["layer_mid"][b, rows])
+        m_tap = host(d["mlp_input"][b, rows])
+        lo_tap = host(d["layer_output"][b, rows])
+        assert rel_err(a_tap[rows], ob.rms_norm(x64[b, rows], W["w_in_norm"], w.eps)) <= BF16_BAR
+        att = ob.attention_sublayer(x64[b], a_tap, mk, W, cfg, rows)
+        assert rel_err(mid_tap, att["layer_mid"]) <= BF16_BAR
+        if "attention_scores" in d:
+            sc = host(d["attention_scores"][b][:, torch.from_numpy(rows).cuda()])
+            kmax = int(rows.max()) + 1
+            check_scores(sc[:, :, :kmax], att["attention_scores"], BF16_BAR)
+            assert np.all(np.isneginf(sc[:, :, kmax:]))
+        assert rel_err(m_tap, ob.mlp_norm(mid_tap, W, cfg)) <= BF16_BAR
+        logits = host(d["router_logits"][b, rows]) if w.mlp == "moe" else None
+        mo = ob.mlp_sublayer(mid_tap, m_tap, W, cfg, router_logits=logits)
+        assert rel_err(lo_tap, mo["layer_output"]) <= BF16_BAR
+        # end to end at the sampled rows, against the bf16 floor
+        r = ob.block_forward(x64[b], mk, W, cfg, rows)
+        emu = em.block_bf16(x64[b], mk, W, cfg, rows)
+        same = np.ones(len(rows), bool)
+        if w.mlp == "moe":
+            gi = np.sort(d["expert_indices"][b, rows].cpu().numpy(), -1)
+            same = (np.all(gi == np.sort(r["expert_indices"], -1), -1) &
+                    np.all(np.sort(emu["expert_indices"], -1) ==
+                           np.sort(r["expert_indices"], -1), -1))
+        y = host(d["y_raw"][b, rows])
+        got = rel_err(y[same], r["layer_output"][same])
+        floor = rel_err(ob.round_bf16(emu["layer_output"][same]), r["layer_output"][same])
+        print(f"[fullsize] {name} b={b}: end-to-end y (gpu, bf16 floor) = "
+              f"({got:.4g}, {floor:.4g}); rows compared {same.sum()}/{len(rows)}", flush=True)
+        assert got <= floor_bar(floor)

@@ -1,0 +1,251 @@
+"""ctypes binding of libblock (include/libblock.h), argument marshalling only.
+
+The names mirror the C ABI: ``blk_create``, ``blk_forward``, ``blk_destroy``,
+``blk_status_str``, ``blk_last_error``, ``blk_abi_version``,
+``blk_workspace_bytes``, and the structs ``blk_config``, ``blk_weights``,
+``blk_tap``, ``blk_taps``, ``blk_io``.  ``Block`` is a small convenience
+wrapper that fills those structs from torch tensors (PyTorch supplies device
+memory and the stream; every step of the block runs in libblock's kernels).
+
+Loading fails loudly if libblock.so has not been built: there is no other
+implementation behind these names.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libblock.so")
+
+BLK_OK, BLK_E_NULL, BLK_E_CONFIG, BLK_E_SHAPE, BLK_E_ALIGN, BLK_E_DTYPE, \
+    BLK_E_OOM, BLK_E_HIP = range(8)
+BLK_F32, BLK_BF16, BLK_I32 = 0, 1, 2
+BLK_MLP_SWIGLU, BLK_MLP_RELU2, BLK_MLP_XIELU, BLK_MLP_MOE = 0, 1, 2, 3
+MLP_KIND = {"swiglu": BLK_MLP_SWIGLU, "relu2": BLK_MLP_RELU2,
+            "xielu": BLK_MLP_XIELU, "moe": BLK_MLP_MOE}
+
+
+class blk_config(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("hidden", C.c_int32), ("num_heads", C.c_int32),
+        ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("mlp_kind", C.c_int32), ("intermediate", C.c_int32),
+        ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+        ("use_rope", C.c_int32), ("qk_norm", C.c_int32),
+        ("sandwich_norm", C.c_int32), ("sliding_window", C.c_int32),
+        ("head_gate_dim", C.c_int32), ("num_experts", C.c_int32),
+        ("top_k", C.c_int32), ("moe_intermediate", C.c_int32),
+        ("num_shared_experts", C.c_int32), ("route_scale", C.c_float),
+        ("xielu_beta", C.c_float), ("xielu_eps", C.c_float),
+        ("max_batch", C.c_int32), ("max_seq", C.c_int32),
+    ]
+
+
+WEIGHT_FIELDS = [
+    "w_in_norm", "w_post_attn_norm", "w_mlp_norm", "w_post_mlp_norm",
+    "wq", "wk", "wv", "wo", "w_q_norm", "w_k_norm", "w_head_gate",
+    "w_gate", "w_up", "w_down",
+]
+WEIGHT_FIELDS_2 = ["w_router", "expert_bias", "w_e_gate", "w_e_up", "w_e_down",
+                   "w_sh_gate", "w_sh_up", "w_sh_down"]
+
+
+class blk_weights(C.Structure):
+    _fields_ = ([(n, C.c_void_p) for n in WEIGHT_FIELDS]
+                + [("xielu_alpha_p_raw", C.c_double),
+                   ("xielu_alpha_n_raw", C.c_double)]
+                + [(n, C.c_void_p) for n in WEIGHT_FIELDS_2])
+
+
+class blk_tap(C.Structure):
+    _fields_ = [("ptr", C.c_void_p), ("dtype", C.c_int32)]
+
+
+TAP_NAMES = ["layer_input", "attention_norm_output", "attention_scores",
+             "layer_mid", "mlp_input", "layer_output", "attention_output",
+             "mlp_output", "router_logits", "expert_indices", "expert_weights"]
+
+
+class blk_taps(C.Structure):
+    _fields_ = [(n, blk_tap) for n in TAP_NAMES]
+
+
+class blk_io(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("attention_mask", C.c_void_p),
+                ("batch", C.c_int32), ("seq", C.c_int32), ("y", C.c_void_p)]
+
+
+class blk_handle(C.Structure):
+    pass
+
+
+_lib = None
+
+
+def load():
+    """Load libblock.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m transformer_decoder_block_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    H = C.POINTER(blk_handle)
+    lib.blk_create.argtypes = [C.POINTER(blk_config), C.POINTER(H)]
+    lib.blk_create.restype = C.c_int
+    lib.blk_forward.argtypes = [H, C.POINTER(blk_io), C.POINTER(blk_weights),
+                                C.POINTER(blk_taps), C.c_void_p]
+    lib.blk_forward.restype = C.c_int
+    lib.blk_destroy.argtypes = [H]
+    lib.blk_destroy.restype = None
+    lib.blk_status_str.argtypes = [C.c_int]
+    lib.blk_status_str.restype = C.c_char_p
+    lib.blk_last_error.argtypes = []
+    lib.blk_last_error.restype = C.c_char_p
+    lib.blk_abi_version.argtypes = []
+    lib.blk_abi_version.restype = C.c_int32
+    lib.blk_workspace_bytes.argtypes = [H]
+    lib.blk_workspace_bytes.restype = C.c_size_t
+    lib.blk_profile_begin.argtypes = [H, C.c_int32]
+    lib.blk_profile_begin.restype = C.c_int
+    lib.blk_profile_end.argtypes = [H, C.c_int32, C.POINTER(C.c_char_p),
+                                    C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+    lib.blk_profile_end.restype = C.c_int32
+    _lib = lib
+    return lib
+
+
+def blk_create(cfg: blk_config):
+    """Returns (status, handle)."""
+    lib = load()
+    h = C.POINTER(blk_handle)()
+    st = lib.blk_create(C.byref(cfg), C.byref(h))
+    return st, h
+
+
+def blk_forward(h, io: blk_io, w: blk_weights, taps, stream: int):
+    lib = load()
+    return lib.blk_forward(h, C.byref(io), C.byref(w),
+                           C.byref(taps) if taps is not None else None,
+                           C.c_void_p(stream))
+
+
+def blk_destroy(h):
+    load().blk_destroy(h)
+
+
+def blk_status_str(s: int) -> str:
+    return load().blk_status_str(s).decode()
+
+
+def blk_last_error() -> str:
+    return load().blk_last_error().decode()
+
+
+def blk_abi_version() -> int:
+    return load().blk_abi_version()
+
+
+def blk_workspace_bytes(h) -> int:
+    return load().blk_workspace_bytes(h)
+
+
+def blk_profile_begin(h, max_forwards: int) -> int:
+    return load().blk_profile_begin(h, max_forwards)
+
+
+def blk_profile_end(h, max_entries: int = 32):
+    """Returns [(name, total_ms, forwards)] or None if profiling was off."""
+    names = (C.c_char_p * max_entries)()
+    tot = (C.c_double * max_entries)()
+    calls = (C.c_int32 * max_entries)()
+    n = load().blk_profile_end(h, max_entries, names, tot, calls)
+    if n < 0:
+        return None
+    return [(names[i].decode(), tot[i], calls[i]) for i in range(n)]
+
+
+class BlockError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{blk_status_str(status)}: {detail}")
+        self.status = status
+
+
+def make_config(w, max_batch=None, max_seq=None) -> blk_config:
+    """blk_config from a workload description (synth.Workload or dict)."""
+    d = w if isinstance(w, dict) else w.as_dict()
+    return blk_config(
+        dtype=BLK_BF16 if d["dtype"] == "bf16" else BLK_F32,
+        hidden=d["H"], num_heads=d["nh"], num_kv_heads=d["nkv"],
+        head_dim=d["hd"], mlp_kind=MLP_KIND[d["mlp"]],
+        intermediate=d.get("I", 0), rms_eps=d["eps"], rope_theta=d["theta"],
+        use_rope=int(d["use_rope"]), qk_norm=int(d["qk_norm"]),
+        sandwich_norm=int(d["sandwich"]), sliding_window=d["window"],
+        head_gate_dim=d["head_gate"], num_experts=d.get("E", 0),
+        top_k=d.get("top_k", 0), moe_intermediate=d.get("I_e", 0),
+        num_shared_experts=d.get("n_shared", 0),
+        route_scale=d.get("route_scale", 1.0),
+        xielu_beta=d.get("xielu_beta", 0.5), xielu_eps=d.get("xielu_eps", -1e-6),
+        max_batch=max_batch or d["B"], max_seq=max_seq or d["S"])
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class Block:
+    """One libblock handle plus the device weights it is called with."""
+
+    def __init__(self, cfg: blk_config, weights: dict):
+        st, h = blk_create(cfg)
+        if st != BLK_OK:
+            raise BlockError(st, blk_last_error())
+        self.cfg = cfg
+        self.h = h
+        self.keep = dict(weights)   # keep tensors alive
+        w = blk_weights()
+        for n in WEIGHT_FIELDS + WEIGHT_FIELDS_2:
+            t = weights.get(n)
+            setattr(w, n, _ptr(t) if t is not None else None)
+        w.xielu_alpha_p_raw = float(weights.get("xielu_alpha_p", 0.0))
+        w.xielu_alpha_n_raw = float(weights.get("xielu_alpha_n", 0.0))
+        self.w = w
+
+    @property
+    def workspace_bytes(self):
+        return blk_workspace_bytes(self.h)
+
+    def forward(self, x, y, mask=None, taps=None, stream=None):
+        """x, y: [B, S, H] device tensors; mask [B, S] int32 or None; taps:
+        dict name -> (tensor, blk dtype).  Enqueues on `stream` (torch
+        stream or raw handle; default: torch's current stream)."""
+        import torch
+        B, S = int(x.shape[0]), int(x.shape[1])
+        io = blk_io(x=x.data_ptr(), attention_mask=_ptr(mask), batch=B, seq=S,
+                    y=y.data_ptr())
+        tp = None
+        if taps:
+            tp = blk_taps()
+            for name, (t, dt) in taps.items():
+                setattr(tp, name, blk_tap(ptr=t.data_ptr(), dtype=dt))
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        elif not isinstance(stream, int):
+            stream = stream.cuda_stream
+        st = blk_forward(self.h, io, self.w, tp, stream)
+        if st != BLK_OK:
+            raise BlockError(st, blk_last_error())
+
+    def close(self):
+        if self.h:
+            blk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

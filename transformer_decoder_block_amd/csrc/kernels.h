@@ -1,0 +1,123 @@
+// Internal interface between the libblock runtime (block.cpp) and the
+// kernel translation units.  Every launcher enqueues on `stream` and
+// returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blk {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// ---------------------------------------------------------------- GEMM
+// C[M, N] = A[M, K] . B[N, K]^T with an epilogue.  A and B in the model
+// dtype, float32 accumulation.
+enum EpiKind : int {
+  EPI_STORE = 0,     // out = acc (float32 or model dtype, see out_f32)
+  EPI_RESID = 1,     // out_f32 = resid + acc; out_model = model(resid + acc);
+                     // out_raw = acc
+  EPI_SWIGLU = 2,    // paired gate/up rows; out = model(silu(g) * u)
+  EPI_RELU2 = 3,     // out = model(relu(acc)^2)
+  EPI_XIELU = 4,     // out = model(xielu(acc))
+  EPI_QKV = 5,       // q/k/v head-major scatter, q/k norm, rotary, gate
+  EPI_MOE_DOWN = 6   // out[row_pair[r]] = model(pair_weight[row_pair[r]] * acc)
+};
+
+struct GemmParams {
+  int M, N, K;           // N: output columns (SWIGLU: neurons; B has 2N rows)
+  const void* A;         // [*, lda]
+  int64_t lda;
+  const int* a_gather;   // optional: logical row r reads A row a_gather[r]
+  uint32_t a_bytes;      // byte size of the A allocation (< 4 GiB)
+  // B: up to four row segments stacked along N (QKV: q, k, v, gate).
+  // Segment s holds rows [seg_end[s-1], seg_end[s]); SWIGLU: seg 0 = gate,
+  // seg 1 = up, both [N, K].
+  const void* B[4];
+  int seg_end[4];
+  int nseg;
+  int64_t ldb;
+  uint32_t b_bytes[4];   // byte size of each segment (of one group)
+  // grouped (MoE): group g owns logical rows [goff[g], goff[g] + gcnt[g])
+  // and reads B[s] + g * b_group_stride.
+  const int* gcnt;
+  const int* goff;
+  int ngroups;
+  int64_t b_group_stride;
+  // epilogue outputs
+  void* out;             // EPI_STORE/SWIGLU/RELU2/XIELU/MOE_DOWN output
+  int64_t ldo;
+  int out_f32;           // EPI_STORE: 1 = float32 output, 0 = model dtype
+  float* out_f32p;       // EPI_RESID: float32 result (may be null)
+  void* out_model;       // EPI_RESID: model-dtype result (may be null)
+  float* out_raw;        // EPI_RESID: the product alone (may be null)
+  const void* resid;     // EPI_RESID: residual [M, ldo]
+  int resid_f32;         //   1 = float32 residual, 0 = model dtype
+  // EPI_XIELU
+  float xa_p, xa_n, xbeta, xeps;
+  // EPI_MOE_DOWN
+  const int* row_pair;
+  const float* pair_weight;
+  // EPI_QKV
+  void* q; void* k; void* vt;   // [B,nh,S,hd], [B,nkv,S,hd], [B,nkv,hd,Sp]
+                                // with Sp = S rounded up to 64
+  float* gate;                  // [M, G] sigmoid of the gate columns
+  int S, nh, nkv, hd, G;
+  int qk_norm, use_rope;
+  const void* q_norm_w; const void* k_norm_w;
+  const float* rope_cos; const float* rope_sin;   // [S_max, hd/2]
+  float eps;
+};
+
+hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
+                hipStream_t stream);
+
+// --------------------------------------------------------------- norms
+// out[t] = model(g * x[t] / sqrt(mean(x[t]^2) + eps)); x float32 or model.
+hipError_t rmsnorm(DType dt, int x_f32, const void* x, const void* g,
+                   void* out, int rows, int H, float eps, hipStream_t s);
+
+// afmoe attention tail: attn = norm_post(o) (o float32), mid = x + attn,
+// m = model(norm_pre(mid)).  attn_out may be null.
+hipError_t norm_add_norm(DType dt, const float* o, const void* x,
+                         const void* g_post, const void* g_pre,
+                         float* attn_out, float* mid, void* m, int rows,
+                         int H, float eps, hipStream_t s);
+
+// MoE tail: raw = sum_k stage[t, k] + shared[t]; mo = norm_post(raw);
+// out = mid + mo -> out_f32 (may be null), y (model dtype).
+hipError_t moe_combine(DType dt, const void* stage, const float* shared,
+                       const float* mid, const void* g_post, int top_k,
+                       float* mlp_out, float* out_f32, void* y, int rows,
+                       int H, float eps, int sandwich, hipStream_t s);
+
+// ----------------------------------------------------------- attention
+struct AttnParams {
+  const void* q; const void* k; const void* vt;   // see EPI_QKV layouts
+  const float* gate;      // [B*S, G] or null
+  const int* mask;        // [B, S] or null
+  void* out;              // [B*S, nh*hd] model dtype
+  int B, S, nh, nkv, hd, window, G;
+  float scale;            // 1/sqrt(hd)
+};
+hipError_t attention(DType dt, const AttnParams& p, hipStream_t s);
+
+// scores[b,h,i,j] = q.k/sqrt(hd) or -inf (tap only)
+hipError_t attention_scores(DType dt, const AttnParams& p, float* scores,
+                            hipStream_t s);
+
+// ----------------------------------------------------------------- MoE
+// logits [T, E] model dtype -> idx [T, k] int32, w [T, k] float32.
+hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T,
+                    int E, int k, float route_scale, int* idx, float* w,
+                    hipStream_t s);
+// Stable token-major dispatch of the T*k (token, slot) pairs by expert:
+// gcnt[E], goff[E], row_token[T*k], row_pair[T*k]; hist is scratch of
+// dispatch_hist_ints(T*k, E) ints.
+hipError_t moe_dispatch(const int* idx, int T, int k, int E, int* gcnt,
+                        int* goff, int* row_token, int* row_pair, int* hist,
+                        hipStream_t s);
+inline int64_t dispatch_hist_ints(int64_t npairs, int E) {
+  return ((npairs + 1023) / 1024) * E;
+}
+
+}  // namespace blk

@@ -7,8 +7,9 @@ bytes.
 
 Recipe (every tensor):
   * generator: ``numpy.random.default_rng([seed, tensor_index, chunk])``,
-    tensor_index from TENSOR_ORDER, chunk = the leading index of an expert
-    stack (0 otherwise);
+    tensor_index from TENSOR_ORDER; a tensor is drawn flattened (row-major)
+    in consecutive chunks of 2^20 elements, chunk = the chunk's index (the
+    chunks are independent streams, so they are drawn in parallel);
   * z = standard normal drawn as float32; value = fp32(mean + std * z)
     (computed in float64, rounded once to float32); for bf16 workloads the
     stored value is that float32 rounded to bfloat16 (nearest, ties to even);
@@ -22,6 +23,7 @@ Recipe (every tensor):
 from __future__ import annotations
 
 import dataclasses
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -145,8 +147,21 @@ def f32_to_bf16_bits(a):
 
 
 def bf16_bits_to_f64(b):
-    u = np.ascontiguousarray(b, np.uint16).astype(np.uint32) << np.uint32(16)
-    return u.view(np.float32).astype(np.float64)
+    b = np.ascontiguousarray(b, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    fb, fo = b.reshape(-1), out.reshape(-1)
+
+    def conv(c):
+        lo, hi = c * CHUNK, min(fb.size, (c + 1) * CHUNK)
+        u = fb[lo:hi].astype(np.uint32) << np.uint32(16)
+        fo[lo:hi] = u.view(np.float32)
+
+    n = (fb.size + CHUNK - 1) // CHUNK
+    if n <= 1:
+        conv(0) if fb.size else None
+    else:
+        list(_pool().map(conv, range(n)))
+    return out
 
 
 def to_f64(a, dtype):
@@ -156,11 +171,33 @@ def to_f64(a, dtype):
     return np.asarray(a, np.float64)
 
 
-def _normal(seed, idx, chunk, shape, mean, std):
-    rng = np.random.default_rng([seed, idx, chunk])
-    z = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
-    v = (z.astype(np.float64) * std + mean).astype(np.float32)
-    return v.reshape(shape)
+CHUNK = 1 << 20
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4
+        _POOL = ThreadPoolExecutor(max(1, min(16, n)))
+    return _POOL
+
+
+def _normal_stored(seed, idx, shape, mean, std, dtype):
+    """The stored values of one N(mean, std) tensor (see the module recipe)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(c):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        rng = np.random.default_rng([seed, idx, c])
+        z = rng.standard_normal(hi - lo, dtype=np.float32)
+        v = (z.astype(np.float64) * std + mean).astype(np.float32)
+        out[lo:hi] = f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+    list(_pool().map(fill, range((n + CHUNK - 1) // CHUNK)))
+    return out.reshape(shape)
 
 
 def _store(v32, dtype):
@@ -209,33 +246,22 @@ def make_weights(w: Workload):
             out[name] = float(np.float32(rng.uniform(0.5, 1.0)))
             continue
         if name == "expert_bias":
-            out[name] = _normal(w.seed, idx, 0, shape, 0.0, 0.1)
+            out[name] = _normal_stored(w.seed, idx, shape, 0.0, 0.1, "f32")
             continue
         if name.startswith("w_") and name.endswith("norm"):
             if w.unit_gains:
-                v = np.ones(shape, np.float32)
+                out[name] = _store(np.ones(shape, np.float32), w.dtype)
             else:
-                v = _normal(w.seed, idx, 0, shape, 1.0, 0.05)
-            out[name] = _store(v, w.dtype)
+                out[name] = _normal_stored(w.seed, idx, shape, 1.0, 0.05, w.dtype)
             continue
-        if len(shape) == 3:
-            st = np.empty(shape, np.uint16 if w.dtype == "bf16" else np.float32)
-            for e in range(shape[0]):
-                st[e] = _store(_normal(w.seed, idx, e, shape[1:], 0.0, 0.02),
-                               w.dtype)
-            out[name] = st
-            continue
-        out[name] = _store(_normal(w.seed, idx, 0, shape, 0.0, 0.02), w.dtype)
+        out[name] = _normal_stored(w.seed, idx, shape, 0.0, 0.02, w.dtype)
     return out
 
 
 def make_x(w: Workload):
     """layer_input [B, S, H] in storage format."""
     idx = TENSOR_ORDER.index("x")
-    x = np.empty((w.B, w.S, w.H), np.uint16 if w.dtype == "bf16" else np.float32)
-    for b in range(w.B):
-        x[b] = _store(_normal(w.seed, idx, b, (w.S, w.H), 0.0, 1.0), w.dtype)
-    return x
+    return _normal_stored(w.seed, idx, (w.B, w.S, w.H), 0.0, 1.0, w.dtype)
 
 
 def make_mask(w: Workload):
