@@ -21,7 +21,7 @@ def call(run, x=None, y=None, B=None, S=None, weights=None, taps=None):
     w = run.w
     x = run.xd if x is None else x
     io = L.blk_io(x=x if isinstance(x, int) else x.data_ptr(), attention_mask=None,
-                  batch=B or w.B, seq=S or w.S,
+                  batch=w.B if B is None else B, seq=w.S if S is None else S,
                   y=y if isinstance(y, int) else y.data_ptr())
     st = L.blk_forward(run.block.h, io, weights or run.block.w, taps,
                        torch.cuda.current_stream().cuda_stream)
