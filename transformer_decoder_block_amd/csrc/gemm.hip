@@ -110,7 +110,9 @@ BLK_COMPUTE_F32(1, 4)
 
 // ------------------------------------------------------------ epilogues
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 __device__ __forceinline__ float xielu_f(float z, float ap, float an, float beta,
                                          float eps) {
@@ -118,13 +120,32 @@ __device__ __forceinline__ float xielu_f(float z, float ap, float an, float beta
   return an * (expm1f(fminf(z, eps)) - z) + beta * z;
 }
 
+// Make this wave's LDS writes visible to its own later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Q/K/V(/gate) epilogue.  A wave owns WM rows (tokens) x FN*32 columns; its
+// columns hold whole heads.  Per head: optional per-head RMSNorm (sum of
+// squares over the head's HD columns, reduced across the 32 lanes that
+// hold them), rotary on the pairs (d, d + HD/2), which sit in the same
+// lane, then the head is staged through this wave's slice of LDS so that
+// the global stores are 16-byte and coalesced: q/k rows [token][d] go to
+// [b, head, s, :], v goes transposed to V^T [b, head, d, s] (keys
+// contiguous, the layout the attention kernel's P.V product reads).
 template <typename T, int HD, int FM, int FN, int WM>
 __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
                                              const GemmParams& p, int row0,
-                                             int col0, int lane) {
+                                             int col0, int lane, T* lds) {
   constexpr int HB = HD / 32;       // 32-wide blocks per head
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int QLD = HD + CH;      // staged q/k row   [WM][QLD]
+  constexpr int VLD = WM + CH;      // staged v^T row   [HD][VLD]
   static_assert(FN % HB == 0, "wave columns must hold whole heads");
   const int cl = lane & 31, hi4 = (lane >> 5) * 4;
+  const int Sp = (p.S + 63) & ~63;  // V^T rows are padded to 64 keys
 #pragma unroll
   for (int hh = 0; hh < FN / HB; ++hh) {
     const int c0 = col0 + hh * HD;
@@ -191,26 +212,70 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
           }
         }
     }
+    if (seg < 2) {
+      // stage [row][d], then store rows of the head contiguously
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-        if (row >= p.M) continue;
-        const int b = row / p.S, s = row % p.S;
-        const int Sp = (p.S + 63) & ~63;  // V^T rows are padded to 64 keys
+        for (int fb = 0; fb < HB; ++fb)
 #pragma unroll
-        for (int fb = 0; fb < HB; ++fb) {
-          const int d = fb * 32 + cl;
-          const T v = from_f32<T>(acc[fm][hh * HB + fb][r]);
-          if (seg == 0)
-            ((T*)p.q)[(((int64_t)b * p.nh + head) * p.S + s) * HD + d] = v;
-          else if (seg == 1)
-            ((T*)p.k)[(((int64_t)b * p.nkv + head) * p.S + s) * HD + d] = v;
-          else
-            ((T*)p.vt)[(((int64_t)b * p.nkv + head) * HD + d) * Sp + s] = v;
+          for (int r = 0; r < 16; ++r) {
+            const int rr = fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
+            lds[rr * QLD + fb * 32 + cl] = from_f32<T>(acc[fm][hh * HB + fb][r]);
+          }
+      wave_lds_sync();
+      T* base = (T*)(seg == 0 ? p.q : p.k);
+      const int nheads = seg == 0 ? p.nh : p.nkv;
+      constexpr int CPRW = HD / CH;  // 16-byte chunks per row
+#pragma unroll 4
+      for (int it = 0; it < WM * CPRW / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int rr = idx / CPRW, ch = idx % CPRW;
+        const int row = row0 + rr;
+        if (row < p.M) {
+          const int b = row / p.S, sp = row % p.S;
+          T* dst = base + (((int64_t)b * nheads + head) * p.S + sp) * HD + ch * CH;
+          *reinterpret_cast<uint4*>(dst) =
+              *reinterpret_cast<const uint4*>(lds + rr * QLD + ch * CH);
         }
       }
+    } else {
+      // stage transposed [d][row], then store key-contiguous runs of V^T
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fb = 0; fb < HB; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            T* dstl = lds + (fb * 32 + cl) * VLD + fm * 32 + i * 8 + hi4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dstl[j] = from_f32<T>(acc[fm][hh * HB + fb][i * 4 + j]);
+          }
+      wave_lds_sync();
+      T* base = (T*)p.vt;
+      constexpr int RCH = WM / CH;  // chunks of CH rows per d
+      const bool s_aligned = (p.S % CH) == 0;
+#pragma unroll 4
+      for (int it = 0; it < HD * RCH / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int d = idx / RCH, rc = idx % RCH;
+        const int r0 = row0 + rc * CH;
+        const T* src = lds + d * VLD + rc * CH;
+        const int b0 = r0 / p.S;
+        if (s_aligned && r0 + CH <= p.M && (r0 + CH - 1) / p.S == b0) {
+          T* dst = base + (((int64_t)b0 * p.nkv + head) * HD + d) * Sp + (r0 % p.S);
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+          for (int e = 0; e < CH; ++e) {
+            const int row = r0 + e;
+            if (row >= p.M) break;
+            const int b = row / p.S;
+            base[(((int64_t)b * p.nkv + head) * HD + d) * Sp + (row % p.S)] = src[e];
+          }
+        }
+      }
+    }
+    wave_lds_sync();  // the next head reuses this wave's LDS slice
   }
 }
 
@@ -224,8 +289,9 @@ gemm_kernel(const GemmParams p) {
                 CPR = TL::CPR, LD = TL::LD, WM = TL::WM, WN = TL::WN,
                 FM = TL::FM, FN = TL::FN, AL = TL::AL, BL = TL::BL;
   constexpr bool PAIRED = (EPI == EPI_SWIGLU);
-  __shared__ __attribute__((aligned(16))) T As[2][BM * LD];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) T smem[2 * (BM + BN) * LD];
+  auto As = [&](int b) { return smem + b * (BM * LD); };
+  auto Bs = [&](int b) { return smem + 2 * BM * LD + b * (BN * LD); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
@@ -285,21 +351,27 @@ gemm_kernel(const GemmParams p) {
   uint32_t b_off[BL];
 #pragma unroll
   for (int i = 0; i < BL; ++i) {
-    const int lrow = tid / CPR + i * (256 / CPR);
+    // rows [lbase, lbase + 32) of the tile are loaded by chunk i; segment
+    // boundaries are multiples of 32 rows, so the segment (and with it the
+    // buffer resource) is uniform across the workgroup.
+    const int lbase = i * (256 / CPR);
+    const int lrow = tid / CPR + lbase;
     int seg, n;
     bool ok;
     if constexpr (PAIRED) {
-      const int w = lrow / WN, rr = lrow % WN, half = WN / 2;
-      n = nt * (BN / 2) + w * half + (rr % half);
-      seg = rr / half;
+      constexpr int half = WN / 2;
+      seg = (lbase % WN) / half;
+      n = nt * (BN / 2) + (lbase / WN) * half + (lrow % WN) % half;
       ok = n < p.N;
     } else {
+      const int nb = nt * BN + lbase;
+      seg = 0;
+      while (seg < p.nseg - 1 && nb >= p.seg_end[seg]) ++seg;
       n = nt * BN + lrow;
       ok = n < p.N;
-      seg = 0;
-      while (seg < p.nseg - 1 && n >= p.seg_end[seg]) ++seg;
       n -= seg ? p.seg_end[seg - 1] : 0;
     }
+    seg = __builtin_amdgcn_readfirstlane(seg);
     rB[i] = __builtin_amdgcn_make_buffer_rsrc((void*)((const T*)p.B[seg] + gofs),
                                               (short)0, p.b_bytes[seg], 0x00020000);
     b_off[i] = ok ? (uint32_t)(((int64_t)n * p.ldb + kc * CH) * sizeof(T))
@@ -323,12 +395,12 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int lrow = tid / CPR + i * (256 / CPR);
-      *reinterpret_cast<uint4*>(&As[buf][lrow * LD + kc * CH]) = ra[i];
+      *reinterpret_cast<uint4*>(As(buf) + lrow * LD + kc * CH) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int lrow = tid / CPR + i * (256 / CPR);
-      *reinterpret_cast<uint4*>(&Bs[buf][lrow * LD + kc * CH]) = rb[i];
+      *reinterpret_cast<uint4*>(Bs(buf) + lrow * LD + kc * CH) = rb[i];
     }
   };
 
@@ -347,7 +419,7 @@ gemm_kernel(const GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
-    compute_tile<T, FM, FN, LD, BK>(acc, As[cur], Bs[cur], wm * WM, wn * WN,
+    compute_tile<T, FM, FN, LD, BK>(acc, As(cur), Bs(cur), wm * WM, wn * WN,
                                     lane);
     if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
@@ -357,10 +429,16 @@ gemm_kernel(const GemmParams p) {
   const int cl = lane & 31, hi4 = (lane >> 5) * 4;
   const int lrow0 = mt * BM + wm * WM;  // tile-local (group-local) row base
   if constexpr (EPI == EPI_QKV) {
+    // each wave stages its heads in its own slice of the (now idle) LDS
+    constexpr int CHT = 16 / sizeof(T);
+    constexpr int SLICE = (WM * (128 + CHT) > 128 * (WM + CHT)) ? WM * (128 + CHT)
+                                                                 : 128 * (WM + CHT);
+    static_assert(4 * SLICE <= 2 * (BM + BN) * LD, "LDS slices fit");
+    T* slice = smem + wave * SLICE;
     if (p.hd == 64)
-      qkv_epilogue<T, 64, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane);
+      qkv_epilogue<T, 64, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
     else
-      qkv_epilogue<T, 128, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane);
+      qkv_epilogue<T, 128, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
     return;
   } else if constexpr (PAIRED) {
     const int ncol0 = nt * (BN / 2) + wn * (WN / 2);
