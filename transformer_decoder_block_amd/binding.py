@@ -92,7 +92,7 @@ def load():
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with "
             "`python -m transformer_decoder_block_amd.build`")
-    lib = C.CDLL(LIB_PATH)
+    lib = C.CDLL(LIB_PATH, mode=os.RTLD_NOW)  # unresolved symbols fail here
     H = C.POINTER(blk_handle)
     lib.blk_create.argtypes = [C.POINTER(blk_config), C.POINTER(H)]
     lib.blk_create.restype = C.c_int

@@ -4,20 +4,30 @@
 //                                         Linear layout [out, in] for B)
 //
 // One workgroup = 4 wavefronts computes a BM x BN tile; each wave owns a
-// (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks.  Operand tiles of
-// 128 bytes of K per row are staged through LDS, double-buffered: the
-// global loads of step k+1 are issued before the MFMAs of step k and land
-// in the other LDS buffer afterwards, so one barrier per K-step suffices.
-// LDS rows are padded by 16 bytes so the 16-byte fragment reads of 16 (or
-// 8) consecutive rows hit distinct banks.
+// (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks.  K is consumed in
+// tiles of 128 bytes per row (64 bf16 / 32 fp32).  Operand tiles go from
+// global memory straight into LDS (buffer_load ... lds: no VGPR staging),
+// double-buffered: the loads of K-tile k+1 are issued right after the
+// barrier that opens K-tile k and land while its MFMAs run, so one barrier
+// per K-tile suffices.  Raw buffer loads return zeros at or past the
+// resource size, which covers ragged M/N edges and the K tail.
+//
+// LDS layout: row r of a tile is 128 contiguous bytes = eight 16-byte
+// chunks; chunk c is stored in slot c ^ (r & 7).  A direct-to-LDS load
+// writes 64 lanes x 16 bytes contiguously, so each lane fetches the global
+// chunk that belongs in its slot; the fragment reads of 8 consecutive rows
+// at one k then fall in 8 different bank groups.
 //
 // bf16: v_mfma_f32_32x32x16_bf16 (lane l holds row l%32, k 8*(l/32)..+7).
 // f32 : v_mfma_f32_32x32x2f32 with the K order inside a 32-wide K tile
 //       permuted so every lane reads 4 consecutive floats per LDS access
 //       (half h of the wave takes k = 16h + 4g + s at step (g, s)); A and B
 //       use the same permutation, so the sum is unchanged.
-// Accumulator layout (both): lane l holds column l%32 and rows
-//       8*(r/4) + 4*(l/32) + r%4 of its 32x32 block, r = 0..15.
+// The B fragment is the MFMA's first operand, so each 32x32 accumulator
+// block holds C^T: lane l owns row l%32 of C and columns
+// 8*(r/4) + 4*(l/32) + r%4, r = 0..15 -- four consecutive columns per
+// group of four registers, stored with one vector write.
+// Fragments of k-step s+1 are read from LDS while the MFMAs of step s run.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,7 +43,7 @@ struct Tile {
   static constexpr int BK = KTile<T>::BK;
   static constexpr int CH = 16 / sizeof(T);   // elements per 16-byte chunk
   static constexpr int CPR = BK / CH;         // chunks per tile row (8)
-  static constexpr int LD = BK + CH;          // padded LDS row (144 bytes)
+  static constexpr int LD = BK;               // LDS row: 128 bytes, swizzled
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int AL = BM * CPR / 256;   // A chunks per thread
@@ -53,60 +63,105 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int nblk) {
                      : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-template <typename T, int FM, int FN, int LD, int BK>
-__device__ __forceinline__ void compute_tile(f32x16 (&acc)[FM][FN],
-                                             const T* As, const T* Bs,
-                                             int arow0, int brow0, int lane);
+// One direct-to-LDS load per lane: 16 bytes at byte offset voff of the
+// buffer land at lds + 16 * lane (lds is the wave's uniform base).
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, const void* lds,
+                                              uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
 
-#define BLK_COMPUTE_BF16(FM_, FN_)                                            \
-  template <>                                                                 \
-  __device__ __forceinline__ void compute_tile<bf16, FM_, FN_, 72, 64>(       \
-      f32x16(&acc)[FM_][FN_], const bf16* As, const bf16* Bs, int arow0,      \
-      int brow0, int lane) {                                                  \
-    const int r = lane & 31, kh = (lane >> 5) * 8;                            \
-    _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                        \
-      bf16x8 af[FM_], bfr[FN_];                                               \
-      _Pragma("unroll") for (int i = 0; i < FM_; ++i) af[i] =                 \
-          *reinterpret_cast<const bf16x8*>(As + (arow0 + i * 32 + r) * 72 +   \
-                                           ks * 16 + kh);                     \
-      _Pragma("unroll") for (int j = 0; j < FN_; ++j) bfr[j] =                \
-          *reinterpret_cast<const bf16x8*>(Bs + (brow0 + j * 32 + r) * 72 +   \
-                                           ks * 16 + kh);                     \
-      _Pragma("unroll") for (int i = 0; i < FM_; ++i)                         \
-          _Pragma("unroll") for (int j = 0; j < FN_; ++j) acc[i][j] =         \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],          \
-                                                      acc[i][j], 0, 0, 0);    \
-    }                                                                         \
+// Address (in elements) of 16-byte chunk c of tile row r.
+template <typename T>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int CH = 16 / sizeof(T);
+  return r * (8 * CH) + ((c ^ (r & 7)) * CH);
+}
+
+template <typename T, int FM, int FN>
+struct Frags;
+template <int FM, int FN>
+struct Frags<bf16, FM, FN> {
+  bf16x8 a[FM], b[FN];
+  // k-step ks (16 wide): lane half hf reads chunk 2 ks + hf
+  __device__ __forceinline__ void load(const bf16* As, const bf16* Bs, int arow0,
+                                       int brow0, int lane, int ks) {
+    const int r = lane & 31, c = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16>(arow0 + i * 32 + r, c));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16>(brow0 + j * 32 + r, c));
   }
-
-BLK_COMPUTE_BF16(4, 4)
-BLK_COMPUTE_BF16(1, 4)
-BLK_COMPUTE_BF16(2, 2)
-BLK_COMPUTE_BF16(2, 4)
-
-#define BLK_COMPUTE_F32(FM_, FN_)                                             \
-  template <>                                                                 \
-  __device__ __forceinline__ void compute_tile<float, FM_, FN_, 36, 32>(      \
-      f32x16(&acc)[FM_][FN_], const float* As, const float* Bs, int arow0,    \
-      int brow0, int lane) {                                                  \
-    const int r = lane & 31, kh = (lane >> 5) * 16;                           \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                           \
-      f32x4 af[FM_], bfr[FN_];                                                \
-      _Pragma("unroll") for (int i = 0; i < FM_; ++i) af[i] =                 \
-          *reinterpret_cast<const f32x4*>(As + (arow0 + i * 32 + r) * 36 +    \
-                                          kh + g * 4);                        \
-      _Pragma("unroll") for (int j = 0; j < FN_; ++j) bfr[j] =                \
-          *reinterpret_cast<const f32x4*>(Bs + (brow0 + j * 32 + r) * 36 +    \
-                                          kh + g * 4);                        \
-      _Pragma("unroll") for (int s = 0; s < 4; ++s)                           \
-          _Pragma("unroll") for (int i = 0; i < FM_; ++i)                     \
-              _Pragma("unroll") for (int j = 0; j < FN_; ++j) acc[i][j] =     \
-                  __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bfr[j][s],   \
-                                                       acc[i][j], 0, 0, 0);   \
-    }                                                                         \
+  __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   }
+};
+template <int FM, int FN>
+struct Frags<float, FM, FN> {
+  f32x4 a[FM], b[FN];
+  // group g (4 k values): lane half hf reads chunk 4 hf + g
+  __device__ __forceinline__ void load(const float* As, const float* Bs, int arow0,
+                                       int brow0, int lane, int g) {
+    const int r = lane & 31, c = 4 * (lane >> 5) + g;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const f32x4*>(As + swz<float>(arow0 + i * 32 + r, c));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const f32x4*>(Bs + swz<float>(brow0 + j * 32 + r, c));
+  }
+  __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j][s], a[i][s], acc[i][j], 0, 0, 0);
+  }
+};
 
-BLK_COMPUTE_F32(1, 4)
+// All MFMAs of one K-tile (4 fragment steps), next step's fragments read
+// while the current step's MFMAs run.
+template <typename T, int FM, int FN>
+__device__ __forceinline__ void compute_tile(f32x16 (&acc)[FM][FN], const T* As,
+                                             const T* Bs, int arow0, int brow0,
+                                             int lane) {
+  Frags<T, FM, FN> f[2];
+  f[0].load(As, Bs, arow0, brow0, lane, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) f[(ks + 1) & 1].load(As, Bs, arow0, brow0, lane, ks + 1);
+    f[ks & 1].mma(acc);
+  }
+  // Schedule: the first step's fragment reads, then each step's MFMAs with
+  // the next step's fragment reads spread between them (without this the
+  // scheduler sinks every read next to its first use and the LDS latency
+  // shows up before each group of MFMAs).
+  constexpr int NMMA = FM * FN * (sizeof(T) == 2 ? 1 : 4);  // MFMAs per step
+  constexpr int NRD = FM + FN;                             // reads per step
+  __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) {
+#pragma unroll
+      for (int r = 0; r < NRD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NMMA / NRD > 0 ? NMMA / NRD : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NMMA > NRD * (NMMA / NRD))
+        __builtin_amdgcn_sched_group_barrier(0x008, NMMA - NRD * (NMMA / NRD), 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, NMMA, 0);
+    }
+  }
+}
 
 // ------------------------------------------------------------ epilogues
 
@@ -127,14 +182,46 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Four consecutive elements of T <-> floats (8-byte bf16, 16-byte fp32).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  uint2 w;
+  w.x = pack2_bf16(a, b);
+  w.y = pack2_bf16(c, d);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load4<bf16>(const bf16* p, float* v) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(w.x << 16);
+  v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16);
+  v[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* v) {
+  const float4 w = *reinterpret_cast<const float4*>(p);
+  v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+}
+
 // Q/K/V(/gate) epilogue.  A wave owns WM rows (tokens) x FN*32 columns; its
-// columns hold whole heads.  Per head: optional per-head RMSNorm (sum of
-// squares over the head's HD columns, reduced across the 32 lanes that
-// hold them), rotary on the pairs (d, d + HD/2), which sit in the same
-// lane, then the head is staged through this wave's slice of LDS so that
-// the global stores are 16-byte and coalesced: q/k rows [token][d] go to
-// [b, head, s, :], v goes transposed to V^T [b, head, d, s] (keys
-// contiguous, the layout the attention kernel's P.V product reads).
+// columns hold whole heads.  Lane l holds token row l%32 of each 32-row
+// block and, per head, half of that row's HD columns (the other half is in
+// lane l^32).  Per head: optional RMSNorm over the head (sum of squares in
+// the lane plus one exchange with lane l^32), rotary on the pairs
+// (d, d + HD/2), which sit in the same lane and register, then the head is
+// staged through this wave's slice of LDS so that the global stores are
+// 16 bytes and coalesced: q/k rows [token][d] go to [b, head, s, :], v goes
+// transposed to V^T [b, head, d, s] (keys contiguous, the layout the
+// attention kernel's P.V product reads).
 template <typename T, int HD, int FM, int FN, int WM>
 __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
                                              const GemmParams& p, int row0,
@@ -155,15 +242,15 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
     const int start = seg ? p.seg_end[seg - 1] : 0;
     if (seg == 3) {  // gate columns: sigmoid, float32 [M, G]
 #pragma unroll
-      for (int fb = 0; fb < HB; ++fb) {
-        const int col = c0 + fb * 32 + cl;
-        if (col >= p.N) continue;
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = row0 + fm * 32 + cl;
+        if (row >= p.M) continue;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+        for (int fb = 0; fb < HB; ++fb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = row0 + fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-            if (row < p.M)
+            const int col = c0 + fb * 32 + (r >> 2) * 8 + hi4 + (r & 3);
+            if (col < p.N)
               p.gate[(int64_t)row * p.G + (col - start)] =
                   1.0f / (1.0f + expf(-acc[fm][hh * HB + fb][r]));
           }
@@ -173,44 +260,54 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
     const int head = (c0 - start) / HD;
     if (seg < 2 && p.qk_norm) {
       const T* gw = (const T*)(seg == 0 ? p.q_norm_w : p.k_norm_w);
-      float gv[HB];
 #pragma unroll
-      for (int fb = 0; fb < HB; ++fb) gv[fb] = to_f32(gw[fb * 32 + cl]);
+      for (int fm = 0; fm < FM; ++fm) {
+        float ss = 0.f;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+        for (int fb = 0; fb < HB; ++fb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float ss = 0.f;
-#pragma unroll
-          for (int fb = 0; fb < HB; ++fb) {
+          for (int r = 0; r < 16; ++r) {
             const float v = acc[fm][hh * HB + fb][r];
             ss += v * v;
           }
-          ss = half_sum(ss);
-          const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + p.eps);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + p.eps);
 #pragma unroll
-          for (int fb = 0; fb < HB; ++fb)
-            acc[fm][hh * HB + fb][r] = gv[fb] * (acc[fm][hh * HB + fb][r] * inv);
-        }
+        for (int fb = 0; fb < HB; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float gv[4];
+            load4(gw + fb * 32 + i * 8 + hi4, gv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[fm][hh * HB + fb][i * 4 + j] = gv[j] * (acc[fm][hh * HB + fb][i * 4 + j] * inv);
+          }
+      }
     }
     if (seg < 2 && p.use_rope) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = row0 + fm * 32 + cl;
+        const int pos = (row < p.M) ? row % p.S : 0;
+        const float* cr = p.rope_cos + (int64_t)pos * (HD / 2);
+        const float* sr = p.rope_sin + (int64_t)pos * (HD / 2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-          const int pos = (row < p.M) ? row % p.S : 0;
+        for (int fb = 0; fb < HB / 2; ++fb)
 #pragma unroll
-          for (int fb = 0; fb < HB / 2; ++fb) {
-            const int d = fb * 32 + cl;
-            const float c = p.rope_cos[pos * (HD / 2) + d];
-            const float s = p.rope_sin[pos * (HD / 2) + d];
-            const float lo = acc[fm][hh * HB + fb][r];
-            const float hi = acc[fm][hh * HB + fb + HB / 2][r];
-            acc[fm][hh * HB + fb][r] = lo * c - hi * s;
-            acc[fm][hh * HB + fb + HB / 2][r] = hi * c + lo * s;
+          for (int i = 0; i < 4; ++i) {
+            float c[4], sn[4];
+            const int d = fb * 32 + i * 8 + hi4;
+            load4(cr + d, c);
+            load4(sr + d, sn);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float lo = acc[fm][hh * HB + fb][i * 4 + j];
+              const float hi = acc[fm][hh * HB + fb + HB / 2][i * 4 + j];
+              acc[fm][hh * HB + fb][i * 4 + j] = lo * c[j] - hi * sn[j];
+              acc[fm][hh * HB + fb + HB / 2][i * 4 + j] = hi * c[j] + lo * sn[j];
+            }
           }
-        }
+      }
     }
     if (seg < 2) {
       // stage [row][d], then store rows of the head contiguously
@@ -219,9 +316,10 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
 #pragma unroll
         for (int fb = 0; fb < HB; ++fb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-            lds[rr * QLD + fb * 32 + cl] = from_f32<T>(acc[fm][hh * HB + fb][r]);
+          for (int i = 0; i < 4; ++i) {
+            const f32x16& a = acc[fm][hh * HB + fb];
+            store4(lds + (fm * 32 + cl) * QLD + fb * 32 + i * 8 + hi4, a[i * 4],
+                   a[i * 4 + 1], a[i * 4 + 2], a[i * 4 + 3]);
           }
       wave_lds_sync();
       T* base = (T*)(seg == 0 ? p.q : p.k);
@@ -246,10 +344,9 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
 #pragma unroll
         for (int fb = 0; fb < HB; ++fb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            T* dstl = lds + (fb * 32 + cl) * VLD + fm * 32 + i * 8 + hi4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dstl[j] = from_f32<T>(acc[fm][hh * HB + fb][i * 4 + j]);
+          for (int r = 0; r < 16; ++r) {
+            const int d = fb * 32 + (r >> 2) * 8 + hi4 + (r & 3);
+            lds[d * VLD + fm * 32 + cl] = from_f32<T>(acc[fm][hh * HB + fb][r]);
           }
       wave_lds_sync();
       T* base = (T*)p.vt;
@@ -289,11 +386,18 @@ gemm_kernel(const GemmParams p) {
                 CPR = TL::CPR, LD = TL::LD, WM = TL::WM, WN = TL::WN,
                 FM = TL::FM, FN = TL::FN, AL = TL::AL, BL = TL::BL;
   constexpr bool PAIRED = (EPI == EPI_SWIGLU);
-  __shared__ __attribute__((aligned(16))) T smem[2 * (BM + BN) * LD];
+  constexpr int CHT = 16 / sizeof(T);
+  // q/k/v epilogue: each wave stages one head in its own LDS slice
+  constexpr int SLICE = (WM * (128 + CHT) > 128 * (WM + CHT)) ? WM * (128 + CHT)
+                                                               : 128 * (WM + CHT);
+  constexpr int MAIN = 2 * (BM + BN) * LD;
+  constexpr int SMEM = (EPI == EPI_QKV && 4 * SLICE > MAIN) ? 4 * SLICE : MAIN;
+  __shared__ __attribute__((aligned(16))) T smem[SMEM];
   auto As = [&](int b) { return smem + b * (BM * LD); };
   auto Bs = [&](int b) { return smem + 2 * BM * LD + b * (BN * LD); };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
   const int n_per_tile = PAIRED ? BN / 2 : BN;
   const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
@@ -325,37 +429,34 @@ gemm_kernel(const GemmParams p) {
     nt = (id % width) / gsz;
   }
 
-  // ---- per-thread global sources.  Operands are read with raw buffer
-  // loads: an offset at or past the resource's byte size returns zeros,
-  // which covers rows past M/N (ragged tiles); the K tail is masked the
-  // same way.  Each thread always reads the same 16-byte column chunk kc
-  // of CPR-chunk rows tid/CPR + 32 i.
-  const int kc = tid % CPR;
+  // ---- direct-to-LDS loads.  Load instruction i of wave w fills tile rows
+  // [8 (4 i + w), +8): lane L writes slot L%8 of row 8(4i+w) + L/8 and so
+  // fetches global chunk (L%8) ^ (row & 7) of that row.  A chunk at or
+  // past the resource size reads as zeros (rows past M/N, the K tail).
+  const int lrow8 = lane >> 3;
+  const int kch = (lane & 7) ^ (lrow8 & 7);  // row & 7 == lane / 8
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, p.a_bytes, 0x00020000);
   uint32_t a_off[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int lrow = tid / CPR + i * (256 / CPR);
+    const int lrow = (4 * i + wave) * 8 + lrow8;
     const int r = mt * BM + lrow;
     int src = row_begin + (r < row_count ? r : 0);
     if (p.a_gather) src = p.a_gather[src];
     a_off[i] = (r < row_count)
-                   ? (uint32_t)(((int64_t)src * p.lda + kc * CH) * sizeof(T))
+                   ? (uint32_t)(((int64_t)src * p.lda + kch * CH) * sizeof(T))
                    : p.a_bytes;
   }
-  // B: the segment (QKV: q/k/v/gate; SWIGLU: gate/up) of chunk i is the
-  // same for the whole workgroup, since segments are 32-row aligned.
+  // B: the segment (QKV: q/k/v/gate; SWIGLU: gate/up) of an 8-row load is
+  // the same for the whole wave, since segments are 32-row aligned.
   const int64_t gofs = GROUPED ? (int64_t)group * p.b_group_stride : 0;
   __amdgpu_buffer_rsrc_t rB[BL];
   uint32_t b_off[BL];
 #pragma unroll
   for (int i = 0; i < BL; ++i) {
-    // rows [lbase, lbase + 32) of the tile are loaded by chunk i; segment
-    // boundaries are multiples of 32 rows, so the segment (and with it the
-    // buffer resource) is uniform across the workgroup.
-    const int lbase = i * (256 / CPR);
-    const int lrow = tid / CPR + lbase;
+    const int lbase = (4 * i + wave) * 8;
+    const int lrow = lbase + lrow8;
     int seg, n;
     bool ok;
     if constexpr (PAIRED) {
@@ -374,34 +475,19 @@ gemm_kernel(const GemmParams p) {
     seg = __builtin_amdgcn_readfirstlane(seg);
     rB[i] = __builtin_amdgcn_make_buffer_rsrc((void*)((const T*)p.B[seg] + gofs),
                                               (short)0, p.b_bytes[seg], 0x00020000);
-    b_off[i] = ok ? (uint32_t)(((int64_t)n * p.ldb + kc * CH) * sizeof(T))
+    b_off[i] = ok ? (uint32_t)(((int64_t)n * p.ldb + kch * CH) * sizeof(T))
                   : p.b_bytes[seg];
   }
-
-  uint4 ra[AL], rb[BL];
-  auto gload = [&](int kt) {
-    const bool kval = kt * BK + kc * CH < p.K;
+  auto issue = [&](int kt, int buf) {
+    const bool kval = kt * BK + kch * CH < p.K;
     const uint32_t ko = kt * BK * sizeof(T);
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rA, kval ? a_off[i] + ko : p.a_bytes, 0, 0));
+      load16_to_lds(rA, As(buf) + (4 * i + wave) * 8 * LD, kval ? a_off[i] + ko : p.a_bytes);
 #pragma unroll
     for (int i = 0; i < BL; ++i)
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rB[i], kval ? b_off[i] + ko : 0xffffffffu, 0, 0));
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < AL; ++i) {
-      const int lrow = tid / CPR + i * (256 / CPR);
-      *reinterpret_cast<uint4*>(As(buf) + lrow * LD + kc * CH) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      const int lrow = tid / CPR + i * (256 / CPR);
-      *reinterpret_cast<uint4*>(Bs(buf) + lrow * LD + kc * CH) = rb[i];
-    }
+      load16_to_lds(rB[i], Bs(buf) + (4 * i + wave) * 8 * LD,
+                    kval ? b_off[i] + ko : 0xffffffffu);
   };
 
   f32x16 acc[FM][FN];
@@ -413,27 +499,23 @@ gemm_kernel(const GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (p.K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    compute_tile<T, FM, FN, LD, BK>(acc, As(cur), Bs(cur), wm * WM, wn * WN,
-                                    lane);
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    // this thread's loads of K-tile kt have landed; after the barrier all
+    // threads' have, and every wave is done reading the other buffer
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+    compute_tile<T, FM, FN>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
   }
+  __syncthreads();  // LDS is free for the epilogue
 
   // ---- epilogue
   const int cl = lane & 31, hi4 = (lane >> 5) * 4;
   const int lrow0 = mt * BM + wm * WM;  // tile-local (group-local) row base
   if constexpr (EPI == EPI_QKV) {
     // each wave stages its heads in its own slice of the (now idle) LDS
-    constexpr int CHT = 16 / sizeof(T);
-    constexpr int SLICE = (WM * (128 + CHT) > 128 * (WM + CHT)) ? WM * (128 + CHT)
-                                                                 : 128 * (WM + CHT);
-    static_assert(4 * SLICE <= 2 * (BM + BN) * LD, "LDS slices fit");
     T* slice = smem + wave * SLICE;
     if (p.hd == 64)
       qkv_epilogue<T, 64, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
@@ -443,60 +525,109 @@ gemm_kernel(const GemmParams p) {
   } else if constexpr (PAIRED) {
     const int ncol0 = nt * (BN / 2) + wn * (WN / 2);
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
+      const int lr = lrow0 + fm * 32 + cl;
+      if (lr >= row_count) continue;
+      T* orow = (T*)p.out + (int64_t)(row_begin + lr) * p.ldo;
 #pragma unroll
-      for (int fn = 0; fn < FN / 2; ++fn) {
-        const int col = ncol0 + fn * 32 + cl;
+      for (int fn = 0; fn < FN / 2; ++fn)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = lrow0 + fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-          if (lr < row_count && col < p.N) {
-            const float g = acc[fm][fn][r], u = acc[fm][fn + FN / 2][r];
-            ((T*)p.out)[(int64_t)(row_begin + lr) * p.ldo + col] =
-                from_f32<T>(silu_f(g) * u);
+        for (int i = 0; i < 4; ++i) {
+          const int col = ncol0 + fn * 32 + i * 8 + hi4;
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[j] = silu_f(acc[fm][fn][i * 4 + j]) * acc[fm][fn + FN / 2][i * 4 + j];
+          if (col + 3 < p.N) {
+            store4(orow + col, v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (col + j < p.N) orow[col + j] = from_f32<T>(v[j]);
           }
         }
-      }
+    }
     return;
   } else {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
+      const int lr = lrow0 + fm * 32 + cl;
+      if (lr >= row_count) continue;
+      const int64_t row = row_begin + lr;
+      int64_t orow = row * p.ldo;
+      float wrow = 1.0f;
+      if constexpr (EPI == EPI_MOE_DOWN) {
+        const int pair = p.row_pair[row];
+        orow = (int64_t)pair * p.ldo;
+        wrow = p.pair_weight[pair];
+      }
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = nt * BN + wn * WN + fn * 32 + cl;
-        if (col >= p.N) continue;
+      for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = lrow0 + fm * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-          if (lr >= row_count) continue;
-          const int64_t row = row_begin + lr;
-          const float v = acc[fm][fn][r];
+        for (int i = 0; i < 4; ++i) {
+          const int col = nt * BN + wn * WN + fn * 32 + i * 8 + hi4;
+          if (col >= p.N) continue;
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = acc[fm][fn][i * 4 + j];
+          const int64_t o = orow + col;
+          const bool full = col + 3 < p.N;
           if constexpr (EPI == EPI_STORE) {
-            if (p.out_f32)
-              ((float*)p.out)[row * p.ldo + col] = v;
-            else
-              ((T*)p.out)[row * p.ldo + col] = from_f32<T>(v);
+            if (full) {
+              if (p.out_f32) store4((float*)p.out + o, v[0], v[1], v[2], v[3]);
+              else store4((T*)p.out + o, v[0], v[1], v[2], v[3]);
+            } else {
+              for (int j = 0; j < 4 && col + j < p.N; ++j) {
+                if (p.out_f32) ((float*)p.out)[o + j] = v[j];
+                else ((T*)p.out)[o + j] = from_f32<T>(v[j]);
+              }
+            }
           } else if constexpr (EPI == EPI_RESID) {
-            const int64_t o = row * p.ldo + col;
-            const float res = p.resid_f32 ? ((const float*)p.resid)[o]
-                                          : to_f32(((const T*)p.resid)[o]);
-            const float s = res + v;
-            if (p.out_f32p) p.out_f32p[o] = s;
-            if (p.out_model) ((T*)p.out_model)[o] = from_f32<T>(s);
-            if (p.out_raw) p.out_raw[o] = v;
-          } else if constexpr (EPI == EPI_RELU2) {
-            const float rl = fmaxf(v, 0.f);
-            ((T*)p.out)[row * p.ldo + col] = from_f32<T>(rl * rl);
-          } else if constexpr (EPI == EPI_XIELU) {
-            ((T*)p.out)[row * p.ldo + col] =
-                from_f32<T>(xielu_f(v, p.xa_p, p.xa_n, p.xbeta, p.xeps));
-          } else if constexpr (EPI == EPI_MOE_DOWN) {
-            const int pair = p.row_pair[row];
-            ((T*)p.out)[(int64_t)pair * p.ldo + col] =
-                from_f32<T>(p.pair_weight[pair] * v);
+            float res[4], sum[4];
+            if (full) {
+              if (p.resid_f32) load4((const float*)p.resid + o, res);
+              else load4((const T*)p.resid + o, res);
+            } else {
+              for (int j = 0; j < 4; ++j)
+                res[j] = (col + j < p.N) ? (p.resid_f32 ? ((const float*)p.resid)[o + j]
+                                                        : to_f32(((const T*)p.resid)[o + j]))
+                                         : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sum[j] = res[j] + v[j];
+            if (full) {
+              if (p.out_f32p) store4(p.out_f32p + o, sum[0], sum[1], sum[2], sum[3]);
+              if (p.out_model) store4((T*)p.out_model + o, sum[0], sum[1], sum[2], sum[3]);
+              if (p.out_raw) store4(p.out_raw + o, v[0], v[1], v[2], v[3]);
+            } else {
+              for (int j = 0; j < 4 && col + j < p.N; ++j) {
+                if (p.out_f32p) p.out_f32p[o + j] = sum[j];
+                if (p.out_model) ((T*)p.out_model)[o + j] = from_f32<T>(sum[j]);
+                if (p.out_raw) p.out_raw[o + j] = v[j];
+              }
+            }
+          } else {
+            float w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if constexpr (EPI == EPI_RELU2) {
+                const float rl = fmaxf(v[j], 0.f);
+                w[j] = rl * rl;
+              } else if constexpr (EPI == EPI_XIELU) {
+                w[j] = xielu_f(v[j], p.xa_p, p.xa_n, p.xbeta, p.xeps);
+              } else {  // EPI_MOE_DOWN
+                w[j] = wrow * v[j];
+              }
+            }
+            if (full) {
+              store4((T*)p.out + o, w[0], w[1], w[2], w[3]);
+            } else {
+              for (int j = 0; j < 4 && col + j < p.N; ++j)
+                ((T*)p.out)[o + j] = from_f32<T>(w[j]);
+            }
           }
         }
-      }
+    }
   }
 }
 
