@@ -4,17 +4,23 @@
 // arcee/apertus notes: query head h reads KV head h / (nh/nkv); sliding
 // window of the afmoe notes; key padding of the support() tables).
 //
-// Flash formulation: one workgroup = 4 waves = 128 queries of one head;
-// wave w owns 32 queries.  Key tiles of 64 keys (K rows and the matching
-// V^T columns) are staged through LDS, double-buffered, and shared by the
-// 4 waves.  Each wave computes the TRANSPOSED score block S^T = K Q^T with
-// 32x32 MFMAs, so a lane holds one query (column l%32) and 32 of the 64
-// keys of the tile in registers; the row max needs one exchange with lane
-// l^32 and the online-softmax state (m, l) is a per-lane scalar.  The
-// probabilities feed O^T += V^T P^T directly from registers: the keys a
-// lane holds become the K index of that MFMA, and the V^T fragment is
-// read from LDS in the same key order.  Softmax uses exp2 with the
-// 1/sqrt(hd) scale folded into log2(e).
+// Flash formulation.  One workgroup = 4 waves = 256 queries of one head;
+// wave w owns 64 queries as two 32-query blocks.  Key tiles of 64 keys (K
+// rows and the matching V^T rows) go from global memory straight into LDS
+// (buffer_load ... lds), double-buffered and XOR-swizzled like the GEMM
+// tiles, and are shared by the 4 waves; every K and V fragment a wave
+// reads from LDS feeds the MFMAs of both of its query blocks.
+//
+// Each wave computes the TRANSPOSED score block S^T = K Q^T with 32x32
+// MFMAs, so a lane holds one query (column l%32) and 32 of the 64 keys of
+// the tile; the row max needs one exchange with lane l^32 and the
+// online-softmax state (m, l) is a per-lane scalar.  The probabilities feed
+// O^T += V^T P^T straight from registers: the keys a lane holds become the
+// K index of that MFMA and the V^T fragment is read in the same key order.
+// exp2 with the 1/sqrt(hd) scale folded into log2(e); the per-key mask
+// (causal edge, window edge, padded keys, keys past the sequence) is two
+// compares per score against per-lane bounds, and the O rescale is
+// skipped when no lane's running max moved.
 //
 // Workgroups are numbered so that the query heads sharing one KV head and
 // one query block are consecutive and land on the same XCD (shared K/V in
@@ -26,17 +32,19 @@
 
 namespace blk {
 
-constexpr int QB = 128;  // queries per workgroup
-constexpr int KT = 64;   // keys per tile
+constexpr int QW = 64;        // queries per wave (two 32-query blocks)
+constexpr int QB = 4 * QW;    // queries per workgroup
+constexpr int KT = 64;        // keys per tile
 
 template <typename T, int HD>
 struct AttnCfg {
-  static constexpr int CH = 16 / sizeof(T);          // elements per 16 bytes
-  static constexpr int KLD = HD + CH;                // K tile row (keys)
-  static constexpr int VLD = KT + CH;                // V^T tile row (dims)
-  static constexpr int KCH = KT * HD / CH / 256;     // K chunks per thread
-  static constexpr int VCH = HD * KT / CH / 256;     // V^T chunks per thread
-  static constexpr int DB = HD / 32;                 // 32-row blocks of O^T
+  static constexpr int CH = 16 / sizeof(T);         // elements per 16 bytes
+  static constexpr int KROW = HD * sizeof(T);       // bytes per K tile row
+  static constexpr int VROW = KT * sizeof(T);       // bytes per V^T tile row
+  static constexpr int KELEMS = KT * HD, VELEMS = HD * KT;
+  static constexpr int KLOADS = KT * KROW / 1024 / 4;   // per wave
+  static constexpr int VLOADS = HD * VROW / 1024 / 4;   // per wave
+  static constexpr int DB = HD / 32;                // 32-row blocks of O^T
 };
 
 __device__ __forceinline__ int xcd_contiguous_a(int bid, int nblk) {
@@ -46,16 +54,33 @@ __device__ __forceinline__ int xcd_contiguous_a(int bid, int nblk) {
                      : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-template <typename T, int HD>
-__global__ void __launch_bounds__(256) attn_kernel(const AttnParams p) {
-  using C = AttnCfg<T, HD>;
-  constexpr int CH = C::CH, KLD = C::KLD, VLD = C::VLD, KCH = C::KCH,
-                VCH = C::VCH, DB = C::DB;
-  __shared__ __attribute__((aligned(16))) T Ks[2][KT * KLD];
-  __shared__ __attribute__((aligned(16))) T Vs[2][HD * VLD];
-  __shared__ int Ms[2][KT];
+// element offset of 16-byte chunk c of row r in a swizzled tile whose rows
+// hold CPR chunks
+template <typename T, int CPR>
+__device__ __forceinline__ int aswz(int r, int c) {
+  constexpr int CH = 16 / sizeof(T);
+  return r * (CPR * CH) + ((c ^ (r & 7)) * CH);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, const void* lds,
+                                           uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <typename T, int HD>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(1, 1)))
+attn_kernel(const AttnParams p) {
+  using C = AttnCfg<T, HD>;
+  constexpr int CH = C::CH, DB = C::DB;
+  constexpr int KCPR = HD / CH, VCPR = KT / CH;
+  __shared__ __attribute__((aligned(16))) T smem[2 * (C::KELEMS + C::VELEMS)];
+  auto Ks = [&](int b) { return smem + b * C::KELEMS; };
+  auto Vs = [&](int b) { return smem + 2 * C::KELEMS + b * C::VELEMS; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cl = lane & 31, hf = lane >> 5;
   const int g = p.nh / p.nkv;
   const int nqb = (p.S + QB - 1) / QB;
@@ -69,242 +94,261 @@ __global__ void __launch_bounds__(256) attn_kernel(const AttnParams p) {
   const int qb = nqb - 1 - qbr;  // heavy blocks first
   const int h = kvh * g + hg;
   const int q0 = qb * QB;
-  const int qw = q0 + wave * 32;  // this wave's first query
-  const int myq = qw + cl;        // this lane's query
+  const int qw = q0 + wave * QW;  // this wave's first query
 
   const T* Qh = (const T*)p.q + ((int64_t)b * p.nh + h) * p.S * HD;
   const T* Kh = (const T*)p.k + ((int64_t)b * p.nkv + kvh) * p.S * HD;
   const int Sp = (p.S + 63) & ~63;  // padded row length of V^T
   const T* Vh = (const T*)p.vt + ((int64_t)b * p.nkv + kvh) * HD * Sp;
   const int* mrow = p.mask ? p.mask + (int64_t)b * p.S : nullptr;
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Kh, (short)0, (uint32_t)((int64_t)p.S * HD * sizeof(T)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Vh, (short)0, (uint32_t)((int64_t)HD * Sp * sizeof(T)), 0x00020000);
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
-  constexpr int QREGS = (sizeof(T) == 2) ? HD / 16 : HD / 8;
+  // ---- Q fragments (B operand of S^T = K Q^T) of both query blocks
+  constexpr int NKS = (sizeof(T) == 2) ? HD / 16 : HD / 8;
   typedef typename std::conditional<sizeof(T) == 2, bf16x8, f32x4>::type QFrag;
-  QFrag qf[QREGS];
-  {
-    const bool ok = myq < p.S;
-    const T* qr = Qh + (int64_t)(ok ? myq : 0) * HD;
+  QFrag qf[2][NKS];
 #pragma unroll
-    for (int i = 0; i < QREGS; ++i) {
-      if constexpr (sizeof(T) == 2) {
-        // step i covers d = 16 i + 8 hf .. +7
-        qf[i] = ok ? *reinterpret_cast<const bf16x8*>(qr + i * 16 + hf * 8) : QFrag{};
-      } else {
-        // group i covers d = hf*HD/2 + 4 i .. +3 (permuted K order)
-        qf[i] = ok ? *reinterpret_cast<const f32x4*>(qr + hf * (HD / 2) + i * 4) : QFrag{};
-      }
+  for (int qi = 0; qi < 2; ++qi) {
+    const int q = qw + qi * 32 + cl;
+    const bool ok = q < p.S;
+    const T* qr = Qh + (int64_t)(ok ? q : 0) * HD;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      if constexpr (sizeof(T) == 2)  // step i: d = 16 i + 8 hf .. +7
+        qf[qi][i] = ok ? *reinterpret_cast<const bf16x8*>(qr + i * 16 + hf * 8) : QFrag{};
+      else                           // group i: d = hf HD/2 + 4 i .. +3
+        qf[qi][i] = ok ? *reinterpret_cast<const f32x4*>(qr + hf * (HD / 2) + i * 4) : QFrag{};
     }
   }
 
-  // ---- key tile range of the workgroup
+  // ---- key tiles of the workgroup
   const int qlast = min(q0 + QB, p.S) - 1;
   const int kt_hi = qlast / KT;
   int kt_lo = 0;
   if (p.window > 0) kt_lo = max(0, q0 - p.window + 1) / KT;
 
-  uint4 rk[KCH], rv[VCH];
-  int rm = 1;
-  auto gload = [&](int kt) {
+  // direct-to-LDS: instruction j of wave w fills bytes [(4j+w) KiB, +1 KiB)
+  // of the tile; lane L writes slot L % (row/16) of its row and fetches the
+  // global chunk that the swizzle puts there
+  auto issue = [&](int kt, int buf) {
     const int k0 = kt * KT;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / (HD / CH), dc = c % (HD / CH);
-      rk[i] = (k0 + key < p.S)
-                  ? *reinterpret_cast<const uint4*>(Kh + (int64_t)(k0 + key) * HD + dc * CH)
-                  : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < C::KLOADS; ++j) {
+      constexpr int RPI = 1024 / C::KROW;  // rows per instruction
+      const int row = (4 * j + wave) * RPI + lane / (C::KROW / 16);
+      const int c = (lane % (C::KROW / 16)) ^ (row & 7);
+      lds_load16(rK, Ks(buf) + (4 * j + wave) * 1024 / sizeof(T),
+                 (uint32_t)(((int64_t)(k0 + row) * HD + c * CH) * sizeof(T)));
     }
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + i * 256;
-      const int d = c / (KT / CH), kc = c % (KT / CH);
-      const int key = k0 + kc * CH;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < p.S) {
-        v = *reinterpret_cast<const uint4*>(Vh + (int64_t)d * Sp + key);
-        if (key + CH > p.S) {  // zero the padding past the sequence
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
-          const int valid = p.S - key;  // 1..CH-1 elements
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (sizeof(T) == 2) {
-              if (2 * e >= valid) w[e] = 0;
-              else if (2 * e + 1 >= valid) w[e] &= 0xffffu;
-            } else {
-              if (e >= valid) w[e] = 0;
-            }
-          }
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-      rv[i] = v;
+    for (int j = 0; j < C::VLOADS; ++j) {
+      constexpr int RPI = 1024 / C::VROW;
+      const int d = (4 * j + wave) * RPI + lane / (C::VROW / 16);
+      const int c = (lane % (C::VROW / 16)) ^ (d & 7);
+      lds_load16(rV, Vs(buf) + (4 * j + wave) * 1024 / sizeof(T),
+                 (uint32_t)(((int64_t)d * Sp + k0 + c * CH) * sizeof(T)));
     }
-    if (tid < KT) {
-      const int key = k0 + tid;
-      rm = (key < p.S) && (!mrow || mrow[key] != 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / (HD / CH), dc = c % (HD / CH);
-      *reinterpret_cast<uint4*>(&Ks[buf][key * KLD + dc * CH]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + i * 256;
-      const int d = c / (KT / CH), kc = c % (KT / CH);
-      *reinterpret_cast<uint4*>(&Vs[buf][d * VLD + kc * CH]) = rv[i];
-    }
-    if (tid < KT) Ms[buf][tid] = rm;
   };
 
-  f32x16 o[DB];
+  f32x16 o[2][DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+  for (int qi = 0; qi < 2; ++qi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qi][i][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = p.scale * 1.4426950408889634f;
 
-  gload(kt_lo);
-  sstore(0);
-  __syncthreads();
+  issue(kt_lo, 0);
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int cur = (kt - kt_lo) & 1;
-    if (kt < kt_hi) gload(kt + 1);
     const int k0 = kt * KT;
-    // does this wave see any key of the tile?
-    const bool active = (qw < p.S) && (k0 <= qw + 31) &&
-                        (p.window <= 0 || k0 + KT - 1 > qw - p.window);
-    if (active) {
-      const T* Kt = Ks[cur];
-      const T* Vt = Vs[cur];
-      // ---- S^T blocks: keys kb*32.. x this wave's 32 queries
-      f32x16 s[2];
+    // keys of the tile that exist and are not padding, one bit per key
+    bool kv = k0 + lane < p.S;
+    if (kv && mrow) kv = mrow[k0 + lane] != 0;
+    const uint64_t kvalid = __ballot(kv);
+    const bool all_valid = kvalid == ~0ull;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's tile loads
+    __syncthreads();
+    if (k0 + KT > p.S) {
+      // keys past the sequence: zero their V^T columns (the padded rows of
+      // V^T hold no data)
+      const int nval = p.S - k0;
+      T* V = Vs(cur);
+      for (int e = tid; e < HD * KT; e += 256) {
+        const int d = e / KT, key = e % KT;
+        if (key >= nval) V[aswz<T, VCPR>(d, key / CH) + key % CH] = from_f32<T>(0.f);
+      }
+      __syncthreads();
+    }
+    if (kt < kt_hi) issue(kt + 1, cur ^ 1);
+
+    // skip the tile when neither of this wave's query blocks sees a key of it
+    {
+      const int qa = qw, qz = qw + 63;  // first and last query of the wave
+      const bool any = (qa < p.S) && (k0 <= qz) &&
+                       (p.window <= 0 || k0 + KT - 1 > qa - p.window);
+      if (!any) continue;
+    }
+    const T* Kt = Ks(cur);
+    const T* Vt = Vs(cur);
+
+    // ---- S^T = K Q^T for both query blocks, K fragments shared
+    f32x16 s[2][2];
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qi][kb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int key = kb * 32 + cl;
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + aswz<T, KCPR>(key, 2 * i + hf));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const T* krow = Kt + (kb * 32 + cl) * KLD;
+          for (int qi = 0; qi < 2; ++qi)
+            s[qi][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qi][i], s[qi][kb], 0, 0, 0);
+        } else {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(
+              Kt + aswz<T, KCPR>(key, hf * (HD / 8) + i));
 #pragma unroll
-        for (int i = 0; i < QREGS; ++i) {
-          if constexpr (sizeof(T) == 2) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + i * 16 + hf * 8);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i], s[kb], 0, 0, 0);
-          } else {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(krow + hf * (HD / 2) + i * 4);
+          for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], qf[i][t], s[kb], 0, 0, 0);
-          }
+            for (int qi = 0; qi < 2; ++qi)
+              s[qi][kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], qf[qi][i][t], s[qi][kb], 0, 0, 0);
         }
       }
-      // ---- mask, scale, online softmax (per lane = per query)
-      float tmax = -INFINITY;
+
+    // ---- mask where needed, online softmax (per lane = per query).  The
+    // probabilities go to a separate register array x; the MFMA results in
+    // s are only read.
+    float x[2][32];
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const int myq = qw + qi * 32 + cl;
+      // key kl of the tile is visible iff lo <= kl <= hi (causal edge and
+      // window edge, relative to k0) and it exists and is not padding
+      const int hi = myq - k0;
+      const int lo = (p.window > 0) ? myq - p.window + 1 - k0 : -KT;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kl = kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-          const int key = k0 + kl;
-          const bool vis = (key <= myq) && Ms[cur][kl] &&
-                           (p.window <= 0 || myq - key < p.window);
-          const float v = vis ? s[kb][r] * sl2 : -INFINITY;
-          s[kb][r] = v;
-          tmax = fmaxf(tmax, v);
+          bool vis = (kl <= hi) && (kl >= lo);
+          if (!all_valid) vis = vis && ((kvalid >> kl) & 1ull);
+          x[qi][kb * 16 + r] = vis ? s[qi][kb][r] : -INFINITY;
         }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) tmax = fmaxf(tmax, x[qi][e]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      const float m_new = fmaxf(m_run[qi], tmax * sl2);
       const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[qi] - msub);  // exp2(-inf) = 0
       float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float pe = fast_exp2(fmaf(x[qi][e], sl2, -msub));
+        x[qi][e] = pe;
+        psum += pe;
+      }
+      l_run[qi] = l_run[qi] * alpha + psum;
+      const bool moved = m_new != m_run[qi];
+      m_run[qi] = m_new;
+      if (__ballot(moved) != 0ull) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qi][i][r] *= alpha;
+      }
+    }
+
+    // ---- O^T += V^T P^T over the 64 keys, V fragments shared
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int kb = st >> 1, i0 = (st & 1) * 2;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pb[qi][j] = (bf16)x[qi][kb * 16 + i0 * 4 + j];
+            pb[qi][4 + j] = (bf16)x[qi][kb * 16 + (i0 + 1) * 4 + j];
+          }
+        const int c = kb * 4 + i0;  // chunk of keys kb*32 + i0*8 .. +7
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + cl;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(Vt + aswz<T, VCPR>(d, c) + hf * 4);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(Vt + aswz<T, VCPR>(d, c + 1) + hf * 4);
+          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi)
+            o[qi][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qi], o[qi][db], 0, 0, 0);
+        }
+      }
+    } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(s[kb][r] - msub);  // exp2(-inf) = 0
-          s[kb][r] = e;
-          psum += e;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      // ---- O^T += V^T P^T over the 64 keys of the tile
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kb = st >> 1, i0 = (st & 1) * 2;
-          bf16x8 pb;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pb[j] = (bf16)s[kb][i0 * 4 + j];
-            pb[4 + j] = (bf16)s[kb][(i0 + 1) * 4 + j];
-          }
-          const int key_a = kb * 32 + i0 * 8 + hf * 4;
+        for (int i = 0; i < 4; ++i) {
+          const int c = kb * 8 + 2 * i + hf;  // keys kb*32 + 8 i + 4 hf .. +3
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const T* vrow = Vt + (db * 32 + cl) * VLD;
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + key_a);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + key_a + 8);
-            const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
+            const f32x4 va = *reinterpret_cast<const f32x4*>(Vt + aswz<T, VCPR>(db * 32 + cl, c));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int qi = 0; qi < 2; ++qi)
+                o[qi][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[j], x[qi][kb * 16 + i * 4 + j],
+                                                                 o[qi][db], 0, 0, 0);
           }
         }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key_a = kb * 32 + i * 8 + hf * 4;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const f32x4 va = *reinterpret_cast<const f32x4*>(Vt + (db * 32 + cl) * VLD + key_a);
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[j], s[kb][i * 4 + j], o[db], 0, 0, 0);
-            }
-          }
-      }
     }
-    if (kt < kt_hi) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   // ---- normalise, gate, store premix [B*S, nh*hd]
-  if (myq >= p.S) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv_l = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  const int64_t tok = (int64_t)b * p.S + myq;
-  float gh = 1.0f;
-  if (p.gate && p.G == p.nh) gh = p.gate[tok * p.G + h];
-  T* orow = (T*)p.out + tok * ((int64_t)p.nh * HD) + h * HD;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qi = 0; qi < 2; ++qi) {
+    const int myq = qw + qi * 32 + cl;
+    const float l_tot = l_run[qi] + __shfl_xor(l_run[qi], 32, 64);
+    if (myq >= p.S) continue;
+    const float inv_l = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+    const int64_t tok = (int64_t)b * p.S + myq;
+    float gh = 1.0f;
+    if (p.gate && p.G == p.nh) gh = p.gate[tok * p.G + h];
+    T* orow = (T*)p.out + tok * ((int64_t)p.nh * HD) + h * HD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = db * 32 + i * 8 + hf * 4;
-      float v[4];
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float gv = gh;
-        if (p.gate && p.G != p.nh) gv = p.gate[tok * p.G + h * HD + d0 + j];
-        v[j] = o[db][i * 4 + j] * inv_l * gv;
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + i * 8 + hf * 4;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float gv = gh;
+          if (p.gate && p.G != p.nh) gv = p.gate[tok * p.G + h * HD + d0 + j];
+          v[j] = o[qi][db][i * 4 + j] * inv_l * gv;
+        }
+        if constexpr (sizeof(T) == 2) {
+          uint2 w;
+          w.x = pack2_bf16(v[0], v[1]);
+          w.y = pack2_bf16(v[2], v[3]);
+          *reinterpret_cast<uint2*>(orow + d0) = w;
+        } else {
+          *reinterpret_cast<float4*>(orow + d0) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
-      if constexpr (sizeof(T) == 2) {
-        uint2 w;
-        w.x = pack2_bf16(v[0], v[1]);
-        w.y = pack2_bf16(v[2], v[3]);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      } else {
-        *reinterpret_cast<float4*>(orow + d0) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
+  }
 }
 
 // The attention_scores tap: q.k / sqrt(hd) where visible, -inf elsewhere.
