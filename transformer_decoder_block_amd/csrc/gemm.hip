@@ -13,10 +13,12 @@
 // resource size, which covers ragged M/N edges and the K tail.
 //
 // LDS layout: row r of a tile is 128 contiguous bytes = eight 16-byte
-// chunks; chunk c is stored in slot c ^ (r & 7).  A direct-to-LDS load
-// writes 64 lanes x 16 bytes contiguously, so each lane fetches the global
-// chunk that belongs in its slot; the fragment reads of 8 consecutive rows
-// at one k then fall in 8 different bank groups.
+// chunks; chunk c is stored in slot c ^ ((r >> 1) & 7).  A direct-to-LDS
+// load writes 64 lanes x 16 bytes contiguously, so each lane fetches the
+// global chunk that belongs in its slot.  With 64 four-byte banks, a
+// 16-byte read by 16 lanes of 16 consecutive rows at one k touches every
+// bank once: even rows fill banks 0-31, odd rows 32-63, and within a
+// parity the 8 rows sit in 8 different slots.
 //
 // bf16: v_mfma_f32_32x32x16_bf16 (lane l holds row l%32, k 8*(l/32)..+7).
 // f32 : v_mfma_f32_32x32x2f32 with the K order inside a 32-wide K tile
@@ -33,23 +35,28 @@
 
 namespace blk {
 
-template <typename T> struct KTile;
-template <> struct KTile<bf16> { static constexpr int BK = 64; };
-template <> struct KTile<float> { static constexpr int BK = 32; };
-
-template <typename T, int BM_, int BN_, int WGM_, int WGN_>
+// Tile shape: BM x BN outputs per workgroup of WGM x WGN waves (4: one per
+// SIMD; 8: two per SIMD), KB bytes of K per row per pipeline stage, NS
+// stages in LDS (NS - 1 in flight).
+template <typename T, int BM_, int BN_, int WGM_, int WGN_, int KB_, int NS_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr int BK = KTile<T>::BK;
+  static constexpr int KB = KB_, NS = NS_;
+  static constexpr int BK = KB / sizeof(T);   // K elements per stage
   static constexpr int CH = 16 / sizeof(T);   // elements per 16-byte chunk
-  static constexpr int CPR = BK / CH;         // chunks per tile row (8)
-  static constexpr int LD = BK;               // LDS row: 128 bytes, swizzled
+  static constexpr int CPR = KB / 16;         // chunks per tile row
+  static constexpr int RPI = 1024 / KB;       // rows per direct-load instruction
+  static constexpr int LD = BK;               // LDS row (KB bytes, swizzled)
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int AL = BM * CPR / 256;   // A chunks per thread
-  static constexpr int BL = BN * CPR / 256;   // B chunks per thread
-  static_assert(WGM * WGN == 4, "4 waves");
+  static constexpr int NW = WGM * WGN;        // waves per workgroup
+  static constexpr int NT = 64 * NW;          // threads per workgroup
+  static constexpr int WPE = NW / 4;          // waves per SIMD
+  static constexpr int AL = BM / RPI / NW;    // A load instructions per wave
+  static constexpr int BL = BN / RPI / NW;    // B load instructions per wave
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(FM >= 1 && FN >= 1, "wave tile >= 32x32");
+  static_assert(AL >= 1 && BL >= 1, "every wave loads");
 };
 
 // Blocks are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8).
@@ -71,28 +78,31 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, const vo
       r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-// Address (in elements) of 16-byte chunk c of tile row r.
-template <typename T>
+// Address (in elements) of 16-byte chunk c of tile row r, rows of KB bytes.
+// 64 four-byte banks span 256 bytes = 256/KB rows; the slot of chunk c is
+// c xor'ed with the row's index among the rows that share banks.
+template <typename T, int KB>
 __device__ __forceinline__ int swz(int r, int c) {
-  constexpr int CH = 16 / sizeof(T);
-  return r * (8 * CH) + ((c ^ (r & 7)) * CH);
+  constexpr int CH = 16 / sizeof(T), CPR = KB / 16, RPB = 256 / KB;
+  return r * (CPR * CH) + ((c ^ ((r / RPB) & (CPR - 1))) * CH);
 }
 
-template <typename T, int FM, int FN>
+template <typename T, int FM, int FN, int KB>
 struct Frags;
-template <int FM, int FN>
-struct Frags<bf16, FM, FN> {
+template <int FM, int FN, int KB>
+struct Frags<bf16, FM, FN, KB> {
+  static constexpr int STEPS = KB / 32;  // 16-wide k-steps per stage
   bf16x8 a[FM], b[FN];
-  // k-step ks (16 wide): lane half hf reads chunk 2 ks + hf
+  // k-step ks: lane half hf reads chunk 2 ks + hf
   __device__ __forceinline__ void load(const bf16* As, const bf16* Bs, int arow0,
                                        int brow0, int lane, int ks) {
     const int r = lane & 31, c = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16>(arow0 + i * 32 + r, c));
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16, KB>(arow0 + i * 32 + r, c));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16>(brow0 + j * 32 + r, c));
+      b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16, KB>(brow0 + j * 32 + r, c));
   }
   __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
 #pragma unroll
@@ -102,19 +112,20 @@ struct Frags<bf16, FM, FN> {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   }
 };
-template <int FM, int FN>
-struct Frags<float, FM, FN> {
+template <int FM, int FN, int KB>
+struct Frags<float, FM, FN, KB> {
+  static constexpr int STEPS = KB / 32;  // groups of 4 k per lane half
   f32x4 a[FM], b[FN];
-  // group g (4 k values): lane half hf reads chunk 4 hf + g
+  // group g: lane half hf reads chunk hf * STEPS + g
   __device__ __forceinline__ void load(const float* As, const float* Bs, int arow0,
                                        int brow0, int lane, int g) {
-    const int r = lane & 31, c = 4 * (lane >> 5) + g;
+    const int r = lane & 31, c = STEPS * (lane >> 5) + g;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const f32x4*>(As + swz<float>(arow0 + i * 32 + r, c));
+      a[i] = *reinterpret_cast<const f32x4*>(As + swz<float, KB>(arow0 + i * 32 + r, c));
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      b[j] = *reinterpret_cast<const f32x4*>(Bs + swz<float>(brow0 + j * 32 + r, c));
+      b[j] = *reinterpret_cast<const f32x4*>(Bs + swz<float, KB>(brow0 + j * 32 + r, c));
   }
   __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
 #pragma unroll
@@ -127,17 +138,19 @@ struct Frags<float, FM, FN> {
   }
 };
 
-// All MFMAs of one K-tile (4 fragment steps), next step's fragments read
-// while the current step's MFMAs run.
-template <typename T, int FM, int FN>
+// All MFMAs of one stage, the next step's fragments read while the current
+// step's MFMAs run.
+template <typename T, int FM, int FN, int KB>
 __device__ __forceinline__ void compute_tile(f32x16 (&acc)[FM][FN], const T* As,
                                              const T* Bs, int arow0, int brow0,
                                              int lane) {
-  Frags<T, FM, FN> f[2];
+  using F = Frags<T, FM, FN, KB>;
+  constexpr int NSTEP = F::STEPS;
+  F f[2];
   f[0].load(As, Bs, arow0, brow0, lane, 0);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks < 3) f[(ks + 1) & 1].load(As, Bs, arow0, brow0, lane, ks + 1);
+  for (int ks = 0; ks < NSTEP; ++ks) {
+    if (ks + 1 < NSTEP) f[(ks + 1) & 1].load(As, Bs, arow0, brow0, lane, ks + 1);
     f[ks & 1].mma(acc);
   }
   // Schedule: the first step's fragment reads, then each step's MFMAs with
@@ -148,8 +161,8 @@ __device__ __forceinline__ void compute_tile(f32x16 (&acc)[FM][FN], const T* As,
   constexpr int NRD = FM + FN;                             // reads per step
   __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks < 3) {
+  for (int ks = 0; ks < NSTEP; ++ks) {
+    if (ks + 1 < NSTEP) {
 #pragma unroll
       for (int r = 0; r < NRD; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, NMMA / NRD > 0 ? NMMA / NRD : 1, 0);
@@ -161,6 +174,13 @@ __device__ __forceinline__ void compute_tile(f32x16 (&acc)[FM][FN], const T* As,
       __builtin_amdgcn_sched_group_barrier(0x008, NMMA, 0);
     }
   }
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone), n < 64
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // ------------------------------------------------------------ epilogues
@@ -379,22 +399,24 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
 // ---------------------------------------------------------------- kernel
 
 template <typename T, class TL, int EPI, bool GROUPED>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(TL::NT, TL::NT),
+                               amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 gemm_kernel(const GemmParams p) {
   constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, CH = TL::CH,
                 CPR = TL::CPR, LD = TL::LD, WM = TL::WM, WN = TL::WN,
-                FM = TL::FM, FN = TL::FN, AL = TL::AL, BL = TL::BL;
+                FM = TL::FM, FN = TL::FN, AL = TL::AL, BL = TL::BL, NS = TL::NS,
+                RPI = TL::RPI, KB = TL::KB;
+  constexpr int RPB = 256 / KB;  // rows that share the 64 banks
   constexpr bool PAIRED = (EPI == EPI_SWIGLU);
   constexpr int CHT = 16 / sizeof(T);
   // q/k/v epilogue: each wave stages one head in its own LDS slice
   constexpr int SLICE = (WM * (128 + CHT) > 128 * (WM + CHT)) ? WM * (128 + CHT)
                                                                : 128 * (WM + CHT);
-  constexpr int MAIN = 2 * (BM + BN) * LD;
-  constexpr int SMEM = (EPI == EPI_QKV && 4 * SLICE > MAIN) ? 4 * SLICE : MAIN;
+  constexpr int MAIN = NS * (BM + BN) * LD;
+  constexpr int SMEM = (EPI == EPI_QKV && TL::NW * SLICE > MAIN) ? TL::NW * SLICE : MAIN;
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
   auto As = [&](int b) { return smem + b * (BM * LD); };
-  auto Bs = [&](int b) { return smem + 2 * BM * LD + b * (BN * LD); };
+  auto Bs = [&](int b) { return smem + NS * BM * LD + b * (BN * LD); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -430,17 +452,20 @@ gemm_kernel(const GemmParams p) {
   }
 
   // ---- direct-to-LDS loads.  Load instruction i of wave w fills tile rows
-  // [8 (4 i + w), +8): lane L writes slot L%8 of row 8(4i+w) + L/8 and so
-  // fetches global chunk (L%8) ^ (row & 7) of that row.  A chunk at or
-  // past the resource size reads as zeros (rows past M/N, the K tail).
-  const int lrow8 = lane >> 3;
-  const int kch = (lane & 7) ^ (lrow8 & 7);  // row & 7 == lane / 8
+  // [RPI (4 i + w), +RPI): lane L writes slot L % CPR of row
+  // RPI (4i+w) + L / CPR and so fetches the global chunk the swizzle puts
+  // there.  A chunk at or past the resource size reads as zeros (rows past
+  // M/N, the K tail).
+  const int lrowi = lane / CPR;
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, p.a_bytes, 0x00020000);
   uint32_t a_off[AL];
+  int a_k[AL];  // first k of the chunk this lane fetches
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int lrow = (4 * i + wave) * 8 + lrow8;
+    const int lrow = (TL::NW * i + wave) * RPI + lrowi;
+    const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
+    a_k[i] = kch * CH;
     const int r = mt * BM + lrow;
     int src = row_begin + (r < row_count ? r : 0);
     if (p.a_gather) src = p.a_gather[src];
@@ -448,15 +473,18 @@ gemm_kernel(const GemmParams p) {
                    ? (uint32_t)(((int64_t)src * p.lda + kch * CH) * sizeof(T))
                    : p.a_bytes;
   }
-  // B: the segment (QKV: q/k/v/gate; SWIGLU: gate/up) of an 8-row load is
-  // the same for the whole wave, since segments are 32-row aligned.
+  // B: the segment (QKV: q/k/v/gate; SWIGLU: gate/up) of one load is the
+  // same for the whole wave, since segments are 32-row aligned.
   const int64_t gofs = GROUPED ? (int64_t)group * p.b_group_stride : 0;
   __amdgpu_buffer_rsrc_t rB[BL];
   uint32_t b_off[BL];
+  int b_k[BL];
 #pragma unroll
   for (int i = 0; i < BL; ++i) {
-    const int lbase = (4 * i + wave) * 8;
-    const int lrow = lbase + lrow8;
+    const int lbase = (TL::NW * i + wave) * RPI;
+    const int lrow = lbase + lrowi;
+    const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
+    b_k[i] = kch * CH;
     int seg, n;
     bool ok;
     if constexpr (PAIRED) {
@@ -479,15 +507,15 @@ gemm_kernel(const GemmParams p) {
                   : p.b_bytes[seg];
   }
   auto issue = [&](int kt, int buf) {
-    const bool kval = kt * BK + kch * CH < p.K;
     const uint32_t ko = kt * BK * sizeof(T);
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      load16_to_lds(rA, As(buf) + (4 * i + wave) * 8 * LD, kval ? a_off[i] + ko : p.a_bytes);
+      load16_to_lds(rA, As(buf) + (TL::NW * i + wave) * RPI * LD,
+                    kt * BK + a_k[i] < p.K ? a_off[i] + ko : p.a_bytes);
 #pragma unroll
     for (int i = 0; i < BL; ++i)
-      load16_to_lds(rB[i], Bs(buf) + (4 * i + wave) * 8 * LD,
-                    kval ? b_off[i] + ko : 0xffffffffu);
+      load16_to_lds(rB[i], Bs(buf) + (TL::NW * i + wave) * RPI * LD,
+                    kt * BK + b_k[i] < p.K ? b_off[i] + ko : 0xffffffffu);
   };
 
   f32x16 acc[FM][FN];
@@ -499,15 +527,21 @@ gemm_kernel(const GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (p.K + BK - 1) / BK;
-  issue(0, 0);
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // this thread's loads of K-tile kt have landed; after the barrier all
-    // threads' have, and every wave is done reading the other buffer
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    const int cur = kt % NS;
+    // this thread's loads of stage kt have landed (the loads of the later
+    // stages may stay in flight); after the barrier all threads' have, and
+    // every wave is done reading the buffer stage kt + NS - 1 refills
+    if (nk - 1 - kt >= NS - 2)
+      wait_vmcnt<(NS - 2) * (AL + BL)>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
-    compute_tile<T, FM, FN>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    compute_tile<T, FM, FN, KB>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
   }
   __syncthreads();  // LDS is free for the epilogue
 
@@ -640,20 +674,22 @@ static hipError_t launch(const GemmParams& p, int max_rows, hipStream_t s) {
   if (GROUPED) {
     const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p.ngroups;
     dim3 grid(max_tiles, num_n);
-    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED>), grid, dim3(TL::NT), 0,
                        s, p);
   } else {
     const int num_m = (p.M + TL::BM - 1) / TL::BM;
     hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED>),
-                       dim3(num_m * num_n), dim3(256), 0, s, p);
+                       dim3(num_m * num_n), dim3(TL::NT), 0, s, p);
   }
   return hipGetLastError();
 }
 
-using TileL = Tile<bf16, 256, 256, 2, 2>;
-using TileQ = Tile<bf16, 128, 256, 2, 2>;
-using TileS = Tile<bf16, 128, 128, 4, 1>;
-using TileF = Tile<float, 128, 128, 4, 1>;
+// 128-byte K stages, two in LDS (a deeper pipeline of 64-byte stages
+// measured slower: the extra barriers cost more than the latency it hides).
+using TileL = Tile<bf16, 256, 256, 2, 4, 128, 2>;
+using TileQ = Tile<bf16, 128, 256, 2, 2, 128, 2>;  // 8 waves spill in the rotary epilogue
+using TileS = Tile<bf16, 128, 128, 4, 1, 128, 2>;
+using TileF = Tile<float, 128, 128, 4, 1, 128, 2>;
 
 template <typename T, class TL>
 static hipError_t dispatch_epi(EpiKind epi, bool grouped, const GemmParams& p,
