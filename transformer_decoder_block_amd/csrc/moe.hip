@@ -12,8 +12,8 @@
 // the slots in descending order.
 //
 // dispatch: the T*k (token, slot) pairs are grouped by expert in token-major
-// order (a stable counting sort), with no atomics: per-chunk histograms,
-// one scan over (expert, chunk), and a per-chunk write pass.
+// order (a stable counting sort), with no atomics: per-chunk histograms, a
+// per-expert scan over the chunks, and a per-chunk write pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -95,69 +95,95 @@ hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T, int 
 
 constexpr int DCHUNK = 1024;  // pairs per dispatch chunk
 
-// hist[c * E + e] = number of pairs of chunk c routed to expert e.
+// hist[e * nchunks + c] = number of pairs of chunk c routed to expert e
+// (integer LDS atomics: the count does not depend on their order).
 __global__ void __launch_bounds__(256) dispatch_count(const int* __restrict__ idx, int npairs,
-                                                      int E, int* __restrict__ hist) {
-  __shared__ int sidx[DCHUNK];
-  const int c = blockIdx.x;
+                                                      int E, int nchunks,
+                                                      int* __restrict__ hist) {
+  __shared__ int cnt[256];
+  const int c = blockIdx.x, t = threadIdx.x;
   const int p0 = c * DCHUNK;
   const int n = min(DCHUNK, npairs - p0);
-  for (int i = threadIdx.x; i < n; i += 256) sidx[i] = idx[p0 + i];
+  cnt[t] = 0;
   __syncthreads();
-  const int e = threadIdx.x;
-  if (e < E) {
-    int cnt = 0;
-    for (int i = 0; i < n; ++i) cnt += (sidx[i] == e);
-    hist[c * E + e] = cnt;
-  }
+  for (int i = t; i < n; i += 256) atomicAdd(&cnt[idx[p0 + i]], 1);
+  __syncthreads();
+  if (t < E) hist[t * nchunks + c] = cnt[t];
 }
 
-// gcnt[e] = total; goff[e] = exclusive scan of gcnt; hist[c*E+e] becomes the
-// first output row of chunk c's pairs of expert e.
+// One block per expert: exclusive scan of its chunk counts in place (the
+// row of the expert's group where chunk c's pairs start) and its total.
 __global__ void __launch_bounds__(256) dispatch_scan(int* __restrict__ hist, int nchunks,
-                                                     int E, int* __restrict__ gcnt,
-                                                     int* __restrict__ goff) {
-  __shared__ int tot[256];
-  const int e = threadIdx.x;
-  int t = 0;
-  if (e < E)
-    for (int c = 0; c < nchunks; ++c) t += hist[c * E + e];
-  tot[e] = (e < E) ? t : 0;
-  __syncthreads();
-  if (e < E) {
-    int off = 0;
-    for (int j = 0; j < e; ++j) off += tot[j];
-    gcnt[e] = t;
-    goff[e] = off;
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = hist[c * E + e];
-      hist[c * E + e] = off;
-      off += h;
+                                                     int* __restrict__ gcnt) {
+  __shared__ int part[256];
+  const int e = blockIdx.x, t = threadIdx.x;
+  int* h = hist + (int64_t)e * nchunks;
+  int carry = 0;
+  for (int base = 0; base < nchunks; base += 256) {
+    const int v = (base + t < nchunks) ? h[base + t] : 0;
+    part[t] = v;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the 256 values
+    for (int o = 1; o < 256; o <<= 1) {
+      const int add = (t >= o) ? part[t - o] : 0;
+      __syncthreads();
+      part[t] += add;
+      __syncthreads();
     }
+    if (base + t < nchunks) h[base + t] = carry + part[t] - v;
+    carry += part[255];
+    __syncthreads();
   }
+  if (t == 0) gcnt[e] = carry;
 }
 
-__global__ void __launch_bounds__(256) dispatch_write(const int* __restrict__ idx, int npairs,
-                                                      int k, int E,
-                                                      const int* __restrict__ hist,
-                                                      int* __restrict__ row_token,
-                                                      int* __restrict__ row_pair) {
-  __shared__ int sidx[DCHUNK];
-  const int c = blockIdx.x;
+// One wavefront per chunk writes the chunk's pairs in token-major order:
+// expert e's pairs of chunk c go to rows goff[e] + hist[e][c] + their rank
+// among the chunk's earlier pairs of e.  The chunk is walked in rounds of
+// 64 consecutive pairs; a pair's rank inside its round is the number of
+// lower lanes holding the same expert.
+__global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx, int npairs,
+                                                     int k, int E, int nchunks,
+                                                     const int* __restrict__ hist,
+                                                     const int* __restrict__ gcnt,
+                                                     int* __restrict__ goff,
+                                                     int* __restrict__ row_token,
+                                                     int* __restrict__ row_pair) {
+  __shared__ int base[256];
+  const int c = blockIdx.x, l = threadIdx.x;
   const int p0 = c * DCHUNK;
   const int n = min(DCHUNK, npairs - p0);
-  for (int i = threadIdx.x; i < n; i += 256) sidx[i] = idx[p0 + i];
-  __syncthreads();
-  const int e = threadIdx.x;
-  if (e < E) {
-    int pos = hist[c * E + e];
-    for (int i = 0; i < n; ++i) {
-      if (sidx[i] == e) {
-        row_pair[pos] = p0 + i;
-        row_token[pos] = (p0 + i) / k;
-        ++pos;
-      }
+  // first row of each expert's group: exclusive scan of the totals
+  if (l == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      base[e] = acc;
+      acc += gcnt[e];
     }
+  }
+  __syncthreads();
+  for (int e = l; e < E; e += 64) {
+    if (c == 0) goff[e] = base[e];
+    base[e] += hist[e * nchunks + c];
+  }
+  __syncthreads();
+  for (int r0 = 0; r0 < n; r0 += 64) {
+    const int i = r0 + l;
+    const bool ok = i < n;
+    const int e = ok ? idx[p0 + i] : -1;
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      rank += (j < l && ej == e) ? 1 : 0;
+    }
+    if (ok) {
+      const int pos = base[e] + rank;
+      row_pair[pos] = p0 + i;
+      row_token[pos] = (p0 + i) / k;
+    }
+    __syncthreads();
+    if (ok) atomicAdd(&base[e], 1);
+    __syncthreads();
   }
 }
 
@@ -165,10 +191,11 @@ hipError_t moe_dispatch(const int* idx, int T, int k, int E, int* gcnt, int* gof
                         int* row_token, int* row_pair, int* hist, hipStream_t s) {
   const int npairs = T * k;
   const int nchunks = (npairs + DCHUNK - 1) / DCHUNK;
-  hipLaunchKernelGGL(dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, npairs, E, hist);
-  hipLaunchKernelGGL(dispatch_scan, dim3(1), dim3(256), 0, s, hist, nchunks, E, gcnt, goff);
-  hipLaunchKernelGGL(dispatch_write, dim3(nchunks), dim3(256), 0, s, idx, npairs, k, E, hist,
-                     row_token, row_pair);
+  hipLaunchKernelGGL(dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, npairs, E, nchunks,
+                     hist);
+  hipLaunchKernelGGL(dispatch_scan, dim3(E), dim3(256), 0, s, hist, nchunks, gcnt);
+  hipLaunchKernelGGL(dispatch_write, dim3(nchunks), dim3(64), 0, s, idx, npairs, k, E,
+                     nchunks, hist, gcnt, goff, row_token, row_pair);
   return hipGetLastError();
 }
 
