@@ -75,6 +75,36 @@ def kernel_work(w, mask):
     return f
 
 
+def csrc_hash():
+    """Short digest of the kernel sources; HBM counter figures taken from
+    an older build no longer describe the kernels and are not reported."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "transformer_decoder_block_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE/WRITE_SIZE
+    counter summary kept in profiles/, or None when there is none for this
+    workload or the kernels have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line[len("traffic-json:"):])
+            if rec.get("csrc_sha256_16") != csrc_hash():
+                return None
+            return rec["traffic_bytes"].get(kernel)
+    return None
+
+
 def total_flops(work):
     return sum(v for kind, v in work.values() if kind == "flop")
 
@@ -115,6 +145,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the timed steps, copy this many MiB device to device "
+                         "once (a kernel of known traffic for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs the block on one GPU; "
@@ -159,6 +192,12 @@ def main():
     wall = time.perf_counter() - t0
     prof = L.blk_profile_end(blk.h) or []
     ms_step = wall * 1e3 / args.steps
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     work = kernel_work(w, mask)
     flops = total_flops(work)
@@ -178,7 +217,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak,
             "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4),
-            "traffic": None, "kernel": dom_name,
+            "traffic": measured_traffic(w.name, dom_name), "kernel": dom_name,
             "flop_per_launch": work[dom_name][1]}
     tokens = w.T
     value = tokens / (ms_step * 1e-3)

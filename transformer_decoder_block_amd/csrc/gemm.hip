@@ -3,8 +3,9 @@
 //   C[M, N] = A[M, K] . B[N, K]^T        (both operands K-contiguous, the
 //                                         Linear layout [out, in] for B)
 //
-// One workgroup = 4 wavefronts computes a BM x BN tile; each wave owns a
-// (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks.  K is consumed in
+// One workgroup of WGM x WGN wavefronts (4: one per SIMD, or 8: two per
+// SIMD) computes a BM x BN tile; each wave owns a (BM/WGM) x (BN/WGN)
+// sub-tile made of 32x32 MFMA blocks.  K is consumed in
 // tiles of 128 bytes per row (64 bf16 / 32 fp32).  Operand tiles go from
 // global memory straight into LDS (buffer_load ... lds: no VGPR staging),
 // double-buffered: the loads of K-tile k+1 are issued right after the
