@@ -351,6 +351,278 @@ attn_kernel(const AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel.  One workgroup = 4 waves = 128 queries of one head; wave w
+// owns 32 queries.  At most 256 registers per wave, so two workgroups share
+// a CU and one's softmax overlaps the other's MFMAs.
+//
+// Per 64-key tile a wave computes S^T = K Q^T (lane = query l%32, 32 of the
+// 64 keys), then the online softmax, then O^T += V^T P^T with P taken
+// straight from the registers.  For that the V^T rows hold the keys of each
+// aligned group of 16 in the order 0-3, 8-11, 4-7, 12-15 (the QKV epilogue
+// writes them so): the 8 keys a lane holds for one 16-key MFMA step are then
+// one 16-byte chunk of the row.
+//
+// Masking is decided per wave and tile from scalars: a tile that every query
+// of the wave sees whole (below the causal edge, inside the window, no
+// padding) takes no mask at all; the others compare each key against the
+// lane's bounds and the tile's padding bits, branch-free.  The running
+// maximum is raised only when a tile's maximum exceeds it by more than
+// 2^TAU_L2 in the exp2 domain (probabilities stay <= 2^TAU_L2), so the O
+// rescale is rare.
+constexpr int BQW = 32;           // queries per wave
+constexpr int BNW = 4;            // waves per workgroup
+constexpr int BQB = BQW * BNW;    // queries per workgroup
+constexpr float TAU_L2 = 8.0f;
+
+template <int HD>
+struct BCfg {
+  static constexpr int KBYTES = KT * HD * 2;       // K tile, rows = keys
+  static constexpr int VBYTES = HD * KT * 2;       // V^T tile, rows = d
+  static constexpr int KLD = KBYTES / 1024 / BNW;  // direct loads per wave
+  static constexpr int VLD = VBYTES / 1024 / BNW;
+  static constexpr int NKS = HD / 16;              // QK k-steps
+  static constexpr int DB = HD / 32;               // 32-row blocks of O^T
+};
+
+// LDS slot of 16-byte chunk c of row r.  K rows of 256 bytes span all 64
+// banks, so 16 consecutive rows need 16 different slots; rows of 128 bytes
+// (K at hd 64, V^T) pair up as even/odd halves of the banks.
+template <int ROWBYTES>
+__device__ __forceinline__ int bslot(int r, int c) {
+  if constexpr (ROWBYTES == 256) return c ^ (r & 15);
+  else return c ^ ((r >> 1) & 7);
+}
+
+// (v of this lane) op (v of lane l^32), in every lane
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int HD>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(const AttnParams p) {
+  using C = BCfg<HD>;
+  constexpr int NKS = C::NKS, DB = C::DB;
+  constexpr int KRB = HD * 2;  // K row bytes
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (C::KBYTES + C::VBYTES)];
+  auto Kb = [&](int b) { return smem + b * C::KBYTES; };
+  auto Vb = [&](int b) { return smem + 2 * C::KBYTES + b * C::VBYTES; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cl = lane & 31, hf = lane >> 5;
+  const int g = p.nh / p.nkv;
+  const int nqb = (p.S + BQB - 1) / BQB;
+
+  // ---- which (b, KV head, query block, head of the group)
+  const int id = xcd_contiguous_a(blockIdx.x, gridDim.x);
+  const int hg = id % g;
+  const int qbr = (id / g) % nqb;
+  const int kvh = (id / (g * nqb)) % p.nkv;
+  const int b = id / (g * nqb * p.nkv);
+  const int qb = nqb - 1 - qbr;  // heavy blocks first
+  const int h = kvh * g + hg;
+  const int q0 = qb * BQB;
+  const int qw = q0 + wave * BQW;           // the wave's first query
+  const int qz = min(qw + BQW, p.S) - 1;    // its last real query
+  const int myq = qw + cl;
+
+  const bf16* Qh = (const bf16*)p.q + ((int64_t)b * p.nh + h) * p.S * HD;
+  const bf16* Kh = (const bf16*)p.k + ((int64_t)b * p.nkv + kvh) * p.S * HD;
+  const int Sp = (p.S + 63) & ~63;
+  const bf16* Vh = (const bf16*)p.vt + ((int64_t)b * p.nkv + kvh) * HD * Sp;
+  const int* mrow = p.mask ? p.mask + (int64_t)b * p.S : nullptr;
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Kh, (short)0, (uint32_t)((int64_t)p.S * HD * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Vh, (short)0, (uint32_t)((int64_t)HD * Sp * 2), 0x00020000);
+
+  // ---- Q fragments: step i holds d = 16 i + 8 hf .. +7 of the lane's query
+  bf16x8 qf[NKS];
+  {
+    const bool ok = myq < p.S;
+    const bf16* qr = Qh + (int64_t)(ok ? myq : 0) * HD + hf * 8;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i)
+      qf[i] = ok ? *reinterpret_cast<const bf16x8*>(qr + i * 16) : bf16x8{};
+  }
+
+  // ---- key tiles of the workgroup
+  const int kt_hi = (min(q0 + BQB, p.S) - 1) / KT;
+  const int kt_lo = (p.window > 0) ? max(0, q0 - p.window + 1) / KT : 0;
+
+  // direct-to-LDS: instruction j of wave w fills bytes [(BNW j + w) KiB, +1)
+  // of the tile; lane L writes slot L % (row/16) of its row and fetches the
+  // global chunk the swizzle puts there.  The padding mask of the tile's
+  // 64 keys is fetched alongside (lane = key).
+  int mnext = 1;
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * KT;
+#pragma unroll
+    for (int j = 0; j < C::KLD; ++j) {
+      constexpr int RPI = 1024 / KRB;
+      const int blk = BNW * j + wave;
+      const int row = blk * RPI + lane / (KRB / 16);
+      const int c = bslot<KRB>(row, lane % (KRB / 16));
+      lds_load16(rK, Kb(buf) + blk * 1024, (uint32_t)(((k0 + row) * HD + c * 8) * 2));
+    }
+#pragma unroll
+    for (int j = 0; j < C::VLD; ++j) {
+      const int blk = BNW * j + wave;
+      const int d = blk * 8 + lane / 8;
+      const int c = bslot<128>(d, lane % 8);
+      lds_load16(rV, Vb(buf) + blk * 1024, (uint32_t)((d * Sp + k0 + c * 8) * 2));
+    }
+    if (mrow) mnext = (k0 + lane < p.S) ? mrow[k0 + lane] : 1;
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale * 1.4426950408889634f;
+
+  issue(kt_lo, 0);
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    const int cur = (kt - kt_lo) & 1;
+    const int k0 = kt * KT;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's tile loads
+    __syncthreads();
+    const uint64_t kvalid = mrow ? __ballot(mnext != 0) : ~0ull;
+    if (k0 + KT > p.S) {
+      // keys past the sequence: zero their (permuted) V^T columns
+      const int nval = p.S - k0;
+      char* V = Vb(cur);
+      for (int e = tid; e < HD * KT; e += 256) {
+        const int d = e / KT, pos = e % KT;
+        // position -> key within an aligned group of 16: swap bits 2 and 3
+        const int key = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1);
+        if (key >= nval) {
+          const int c = bslot<128>(d, pos / 8);
+          *reinterpret_cast<bf16*>(V + d * 128 + c * 16 + (pos % 8) * 2) = (bf16)0.f;
+        }
+      }
+      __syncthreads();
+    }
+    if (kt < kt_hi) issue(kt + 1, cur ^ 1);
+
+    // wave-uniform tile class
+    const bool any = (qw < p.S) && (k0 <= qz) &&
+                     (p.window <= 0 || k0 + KT - 1 >= qw - p.window + 1);
+    if (!any) continue;
+    const bool full = (k0 + KT - 1 <= qw) &&
+                      (p.window <= 0 || k0 >= qz - p.window + 1) && (kvalid == ~0ull);
+
+    // ---- S^T = K Q^T: two 32-key blocks
+    const char* Kt = Kb(cur);
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(
+          Kt + cl * KRB + bslot<KRB>(cl, 2 * i + hf) * 16);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(
+          Kt + (32 + cl) * KRB + bslot<KRB>(32 + cl, 2 * i + hf) * 16);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[i], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[i], s1, 0, 0, 0);
+    }
+    // lane holds keys kb*32 + 8 (r/4) + 4 hf + r%4 of its query
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { x[r] = s0[r]; x[16 + r] = s1[r]; }
+    if (!full) {
+      const int hi = myq - k0;
+      const int lo = (p.window > 0) ? myq - p.window + 1 - k0 : -KT;
+      const uint32_t w0 = (uint32_t)(kvalid >> (4 * hf));
+      const uint32_t w1 = (uint32_t)(kvalid >> (32 + 4 * hf));
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int r = e & 15;
+        const int kl = (e >> 4) * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+        const uint32_t bit = ((e < 16 ? w0 : w1) >> ((r >> 2) * 8 + (r & 3))) & 1u;
+        const bool vis = (kl <= hi) & (kl >= lo) & (bit != 0u);
+        x[e] = vis ? x[e] : -INFINITY;
+      }
+    }
+
+    // ---- online softmax, one query per lane (keys split with lane l^32)
+    float tmax = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) tmax = fmaxf(tmax, x[e]);
+    const float mt = xhalf_max(tmax) * sl2;
+    if (__ballot(mt > m_run + TAU_L2) != 0ull) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      m_run = m_new;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      x[e] = fast_exp2(fmaf(x[e], sl2, -msub));
+      psum += x[e];
+    }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T, 16 keys per step
+    const char* Vt = Vb(cur);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 pb;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pb[t] = (bf16)x[j * 8 + t];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + cl;
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+            Vt + d * 128 + bslot<128>(d, 2 * j + hf) * 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- normalise, gate, store premix [B*S, nh*hd]
+  const float l_tot = xhalf_sum(l_run);
+  if (myq >= p.S) return;
+  const float inv_l = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  const int64_t tok = (int64_t)b * p.S + myq;
+  float gh = 1.0f;
+  if (p.gate && p.G == p.nh) gh = p.gate[tok * p.G + h];
+  bf16* orow = (bf16*)p.out + tok * ((int64_t)p.nh * HD) + h * HD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = db * 32 + i * 8 + hf * 4;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float gv = gh;
+        if (p.gate && p.G != p.nh) gv = p.gate[tok * p.G + h * HD + d0 + j];
+        v[j] = o[db][i * 4 + j] * inv_l * gv;
+      }
+      uint2 w;
+      w.x = pack2_bf16(v[0], v[1]);
+      w.y = pack2_bf16(v[2], v[3]);
+      *reinterpret_cast<uint2*>(orow + d0) = w;
+    }
+}
+
 // The attention_scores tap: q.k / sqrt(hd) where visible, -inf elsewhere.
 template <typename T, int HD>
 __global__ void __launch_bounds__(256) scores_kernel(const AttnParams p, float* scores) {
@@ -381,9 +653,17 @@ static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HD>
+static hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t s) {
+  const int nqb = (p.S + BQB - 1) / BQB;
+  const int nblk = p.B * p.nh * nqb;
+  hipLaunchKernelGGL((attn_bf16_kernel<HD>), dim3(nblk), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t attention(DType dt, const AttnParams& p, hipStream_t s) {
   if (dt == DType::BF16)
-    return p.hd == 64 ? launch_attn<bf16, 64>(p, s) : launch_attn<bf16, 128>(p, s);
+    return p.hd == 64 ? launch_attn_bf16<64>(p, s) : launch_attn_bf16<128>(p, s);
   return p.hd == 64 ? launch_attn<float, 64>(p, s) : launch_attn<float, 128>(p, s);
 }
 

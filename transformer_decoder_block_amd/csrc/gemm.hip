@@ -370,9 +370,14 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
             lds[d * VLD + fm * 32 + cl] = from_f32<T>(acc[fm][hh * HB + fb][r]);
           }
       wave_lds_sync();
+      // bf16: within each aligned group of 16 keys the row holds keys
+      // 0-3, 8-11, 4-7, 12-15 (position and key differ by a swap of bits
+      // 2 and 3), the order in which the attention kernel's P.V step
+      // consumes them; float rows keep the natural order.
+      constexpr bool PERM = sizeof(T) == 2;
       T* base = (T*)p.vt;
-      constexpr int RCH = WM / CH;  // chunks of CH rows per d
-      const bool s_aligned = (p.S % CH) == 0;
+      constexpr int RCH = WM / CH;  // chunks of CH positions per d
+      const bool s_aligned = PERM ? (p.S % 16) == 0 : (p.S % CH) == 0;
 #pragma unroll 4
       for (int it = 0; it < HD * RCH / 64; ++it) {
         const int idx = it * 64 + lane;
@@ -382,13 +387,23 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
         const int b0 = r0 / p.S;
         if (s_aligned && r0 + CH <= p.M && (r0 + CH - 1) / p.S == b0) {
           T* dst = base + (((int64_t)b0 * p.nkv + head) * HD + d) * Sp + (r0 % p.S);
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+          if constexpr (PERM) {
+            // positions rc*8 .. +7 hold keys (local) rc*8 + {0..3, 8..11}
+            // for even rc and rc*8 + {-4..-1, 4..7} for odd rc
+            const int odd = rc & 1;
+            const uint2 lo = *reinterpret_cast<const uint2*>(src - 4 * odd);
+            const uint2 hi = *reinterpret_cast<const uint2*>(src + 8 - 4 * odd);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          } else {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+          }
         } else {
           for (int e = 0; e < CH; ++e) {
             const int row = r0 + e;
             if (row >= p.M) break;
-            const int b = row / p.S;
-            base[(((int64_t)b * p.nkv + head) * HD + d) * Sp + (row % p.S)] = src[e];
+            const int b = row / p.S, sk = row % p.S;
+            const int pos = PERM ? ((sk & ~12) | ((sk & 4) << 1) | ((sk & 8) >> 1)) : sk;
+            base[(((int64_t)b * p.nkv + head) * HD + d) * Sp + pos] = src[e];
           }
         }
       }
