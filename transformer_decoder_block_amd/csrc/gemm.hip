@@ -327,6 +327,9 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
               acc[fm][hh * HB + fb][i * 4 + j] = lo * c[j] - hi * sn[j];
               acc[fm][hh * HB + fb + HB / 2][i * 4 + j] = hi * c[j] + lo * sn[j];
             }
+            // keep the table loads of later groups from being hoisted here
+            // (their registers would all be live at once)
+            __builtin_amdgcn_sched_barrier(0);
           }
       }
     }
@@ -414,7 +417,7 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
 
 // ---------------------------------------------------------------- kernel
 
-template <typename T, class TL, int EPI, bool GROUPED>
+template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
 __global__ void __attribute__((amdgpu_flat_work_group_size(TL::NT, TL::NT),
                                amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 gemm_kernel(const GemmParams p) {
@@ -567,10 +570,7 @@ gemm_kernel(const GemmParams p) {
   if constexpr (EPI == EPI_QKV) {
     // each wave stages its heads in its own slice of the (now idle) LDS
     T* slice = smem + wave * SLICE;
-    if (p.hd == 64)
-      qkv_epilogue<T, 64, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
-    else
-      qkv_epilogue<T, 128, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
+    qkv_epilogue<T, HDQ, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
     return;
   } else if constexpr (PAIRED) {
     const int ncol0 = nt * (BN / 2) + wn * (WN / 2);
@@ -683,18 +683,18 @@ gemm_kernel(const GemmParams p) {
 
 // ------------------------------------------------------------ launchers
 
-template <typename T, class TL, int EPI, bool GROUPED>
+template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
 static hipError_t launch(const GemmParams& p, int max_rows, hipStream_t s) {
   const int n_per_tile = (EPI == EPI_SWIGLU) ? TL::BN / 2 : TL::BN;
   const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
   if (GROUPED) {
     const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p.ngroups;
     dim3 grid(max_tiles, num_n);
-    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED>), grid, dim3(TL::NT), 0,
+    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), grid, dim3(TL::NT), 0,
                        s, p);
   } else {
     const int num_m = (p.M + TL::BM - 1) / TL::BM;
-    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED>),
+    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>),
                        dim3(num_m * num_n), dim3(TL::NT), 0, s, p);
   }
   return hipGetLastError();
@@ -703,7 +703,7 @@ static hipError_t launch(const GemmParams& p, int max_rows, hipStream_t s) {
 // 128-byte K stages, two in LDS (a deeper pipeline of 64-byte stages
 // measured slower: the extra barriers cost more than the latency it hides).
 using TileL = Tile<bf16, 256, 256, 2, 4, 128, 2>;
-using TileQ = Tile<bf16, 128, 256, 2, 2, 128, 2>;  // 8 waves spill in the rotary epilogue
+using TileQ = Tile<bf16, 256, 256, 4, 2, 128, 2>;  // 64x128 wave tiles: whole heads per wave
 using TileS = Tile<bf16, 128, 128, 4, 1, 128, 2>;
 using TileF = Tile<float, 128, 128, 4, 1, 128, 2>;
 
@@ -724,7 +724,10 @@ static hipError_t dispatch_epi(EpiKind epi, bool grouped, const GemmParams& p,
     case EPI_RELU2: return launch<T, TL, EPI_RELU2, false>(p, max_rows, s);
     case EPI_XIELU: return launch<T, TL, EPI_XIELU, false>(p, max_rows, s);
     case EPI_QKV:
-      if constexpr (TL::FM <= 2) return launch<T, TL, EPI_QKV, false>(p, max_rows, s);
+      if constexpr (TL::FM <= 2) {
+        if (p.hd == 64) return launch<T, TL, EPI_QKV, false, 64>(p, max_rows, s);
+        return launch<T, TL, EPI_QKV, false, 128>(p, max_rows, s);
+      }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -738,9 +741,9 @@ hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
   // workgroups; the 128x128 tile otherwise.
   const int n_per = (epi == EPI_SWIGLU) ? 128 : 256;
   if (epi == EPI_QKV) {
-    // the q/k norm + rotary epilogue needs the register room of a
-    // 64-row wave tile
-    const long tiles_q = (long)((max_rows + 127) / 128) * ((p.N + 255) / 256);
+    // the q/k norm + rotary epilogue needs whole heads in a wave: 64 x 128
+    // wave tiles
+    const long tiles_q = (long)((max_rows + 255) / 256) * ((p.N + 255) / 256);
     if (tiles_q >= 256) return dispatch_epi<bf16, TileQ>(epi, grouped, p, max_rows, s);
     return dispatch_epi<bf16, TileS>(epi, grouped, p, max_rows, s);
   }
