@@ -68,6 +68,11 @@ static void prof_mark(blk_handle* h, const char* name, hipStream_t s) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Row stride of the dense MLP's neuron buffer: the width rounded up to 64
+// elements, so that every 128-byte K stage of the down projection's A rows
+// is one cache line (the pad columns are never read: K stays the width).
+static size_t neuron_ld(int I) { return ((size_t)I + 63) & ~(size_t)63; }
+
 static blk_status check_config(const blk_config* c) {
   if (c->dtype != BLK_F32 && c->dtype != BLK_BF16)
     return fail(BLK_E_CONFIG, "dtype must be BLK_F32 or BLK_BF16");
@@ -174,7 +179,7 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
   add((void**)&h->mid, T * H * 4);
   add(&h->m, T * H * es);
   if (!moe) {
-    add(&h->neur, T * c.intermediate * es);
+    add(&h->neur, T * neuron_ld(c.intermediate) * es);
     if (c.sandwich_norm) add((void**)&h->mlp_raw, T * H * 4);
   } else {
     const size_t E = c.num_experts;
@@ -544,7 +549,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     p.a_bytes = bytes32((size_t)T * H * es);
     p.ldb = H;
     p.out = h->neur;
-    p.ldo = I;
+    p.ldo = (int64_t)neuron_ld(I);
     EpiKind epi;
     if (c.mlp_kind == BLK_MLP_SWIGLU) {
       p.B[0] = w->w_gate;
@@ -575,8 +580,8 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     d.N = H;
     d.K = I;
     d.A = h->neur;
-    d.lda = I;
-    d.a_bytes = bytes32((size_t)T * I * es);
+    d.lda = (int64_t)neuron_ld(I);
+    d.a_bytes = bytes32((size_t)T * neuron_ld(I) * es);
     d.B[0] = w->w_down;
     d.seg_end[0] = H;
     d.nseg = 1;
