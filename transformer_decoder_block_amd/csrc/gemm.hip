@@ -279,72 +279,65 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
       continue;
     }
     const int head = (c0 - start) / HD;
-    if (seg < 2 && p.qk_norm) {
+    if (seg < 2) {
+      // Per row: optional RMSNorm over the head, then rotary on the pairs
+      // (d, d + HD/2), each output computed from acc and written straight
+      // into the staging rows [row][d] (acc itself is never modified: an
+      // in-place update under a condition makes the compiler keep a second
+      // copy of the accumulators).  Where norm or rotary is off, the value
+      // is passed through unchanged.
+      const bool do_norm = p.qk_norm != 0, do_rope = p.use_rope != 0;
       const T* gw = (const T*)(seg == 0 ? p.q_norm_w : p.k_norm_w);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        float ss = 0.f;
+        float inv = 1.0f;
+        if (do_norm) {
+          float ss = 0.f;
 #pragma unroll
-        for (int fb = 0; fb < HB; ++fb)
+          for (int fb = 0; fb < HB; ++fb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float v = acc[fm][hh * HB + fb][r];
-            ss += v * v;
-          }
-        ss += __shfl_xor(ss, 32, 64);
-        const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + p.eps);
-#pragma unroll
-        for (int fb = 0; fb < HB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float gv[4];
-            load4(gw + fb * 32 + i * 8 + hi4, gv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[fm][hh * HB + fb][i * 4 + j] = gv[j] * (acc[fm][hh * HB + fb][i * 4 + j] * inv);
-          }
-      }
-    }
-    if (seg < 2 && p.use_rope) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
+            for (int r = 0; r < 16; ++r) {
+              const float v = acc[fm][hh * HB + fb][r];
+              ss += v * v;
+            }
+          ss += __shfl_xor(ss, 32, 64);
+          inv = 1.0f / sqrtf(ss * (1.0f / HD) + p.eps);
+        }
         const int row = row0 + fm * 32 + cl;
         const int pos = (row < p.M) ? row % p.S : 0;
         const float* cr = p.rope_cos + (int64_t)pos * (HD / 2);
         const float* sr = p.rope_sin + (int64_t)pos * (HD / 2);
+        T* srow = lds + (fm * 32 + cl) * QLD;
 #pragma unroll
         for (int fb = 0; fb < HB / 2; ++fb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float c[4], sn[4];
-            const int d = fb * 32 + i * 8 + hi4;
-            load4(cr + d, c);
-            load4(sr + d, sn);
+            const int d = fb * 32 + i * 8 + hi4;  // low member of the pairs
+            float glo[4] = {1.f, 1.f, 1.f, 1.f}, ghi[4] = {1.f, 1.f, 1.f, 1.f};
+            if (do_norm) {
+              load4(gw + d, glo);
+              load4(gw + d + HD / 2, ghi);
+            }
+            float c[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+            if (do_rope) {
+              load4(cr + d, c);
+              load4(sr + d, sn);
+            }
+            float olo[4], ohi[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float lo = acc[fm][hh * HB + fb][i * 4 + j];
-              const float hi = acc[fm][hh * HB + fb + HB / 2][i * 4 + j];
-              acc[fm][hh * HB + fb][i * 4 + j] = lo * c[j] - hi * sn[j];
-              acc[fm][hh * HB + fb + HB / 2][i * 4 + j] = hi * c[j] + lo * sn[j];
+              const float lo = glo[j] * (acc[fm][hh * HB + fb][i * 4 + j] * inv);
+              const float hi = ghi[j] * (acc[fm][hh * HB + fb + HB / 2][i * 4 + j] * inv);
+              olo[j] = do_rope ? lo * c[j] - hi * sn[j] : lo;
+              ohi[j] = do_rope ? hi * c[j] + lo * sn[j] : hi;
             }
+            store4(srow + d, olo[0], olo[1], olo[2], olo[3]);
+            store4(srow + d + HD / 2, ohi[0], ohi[1], ohi[2], ohi[3]);
             // keep the table loads of later groups from being hoisted here
             // (their registers would all be live at once)
             __builtin_amdgcn_sched_barrier(0);
           }
       }
-    }
-    if (seg < 2) {
-      // stage [row][d], then store rows of the head contiguously
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fb = 0; fb < HB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x16& a = acc[fm][hh * HB + fb];
-            store4(lds + (fm * 32 + cl) * QLD + fb * 32 + i * 8 + hi4, a[i * 4],
-                   a[i * 4 + 1], a[i * 4 + 2], a[i * 4 + 3]);
-          }
       wave_lds_sync();
       T* base = (T*)(seg == 0 ? p.q : p.k);
       const int nheads = seg == 0 ? p.nh : p.nkv;
