@@ -439,8 +439,12 @@ gemm_kernel(const GemmParams p) {
   // ---- which tile
   int mt, nt, row_begin = 0, row_count = p.M, group = 0;
   if constexpr (GROUPED) {
-    int t = blockIdx.x;
-    nt = blockIdx.y;
+    // one dimension: consecutive ids (which the renumbering keeps on one
+    // XCD) are the N tiles of one M tile, so the gathered A rows are read
+    // once and an expert's weights are shared by its M tiles in that L2
+    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+    int t = id / num_n;
+    nt = id % num_n;
     int g = 0;
     for (; g < p.ngroups; ++g) {
       const int tiles = (p.gcnt[g] + BM - 1) / BM;
@@ -682,9 +686,8 @@ static hipError_t launch(const GemmParams& p, int max_rows, hipStream_t s) {
   const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
   if (GROUPED) {
     const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p.ngroups;
-    dim3 grid(max_tiles, num_n);
-    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), grid, dim3(TL::NT), 0,
-                       s, p);
+    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(max_tiles * num_n),
+                       dim3(TL::NT), 0, s, p);
   } else {
     const int num_m = (p.M + TL::BM - 1) / TL::BM;
     hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>),
