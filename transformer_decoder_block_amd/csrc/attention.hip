@@ -353,8 +353,9 @@ attn_kernel(const AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel.  One workgroup = 4 waves = 128 queries of one head; wave w
-// owns 32 queries.  At most 256 registers per wave, so two workgroups share
-// a CU and one's softmax overlaps the other's MFMAs.
+// owns 32 queries.  Registers are capped so that two workgroups (head_dim
+// 128) or three (head_dim 64) share a CU and one's softmax overlaps the
+// others' MFMAs.
 //
 // Per 64-key tile a wave computes S^T = K Q^T (lane = query l%32, 32 of the
 // 64 keys), then the online softmax, then O^T += V^T P^T with P taken
@@ -404,9 +405,10 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// head_dim 64 needs fewer registers and half the LDS: three workgroups per CU
 template <int HD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(2, 2)))
+                               amdgpu_waves_per_eu(HD == 64 ? 3 : 2, HD == 64 ? 3 : 2)))
 attn_bf16_kernel(const AttnParams p) {
   using C = BCfg<HD>;
   constexpr int NKS = C::NKS, DB = C::DB;
