@@ -21,15 +21,17 @@
 // bank once: even rows fill banks 0-31, odd rows 32-63, and within a
 // parity the 8 rows sit in 8 different slots.
 //
-// bf16: v_mfma_f32_32x32x16_bf16 (lane l holds row l%32, k 8*(l/32)..+7).
+// bf16: v_mfma_f32_16x16x32_bf16 (lane l holds row l%16, k 8*(l/16)..+7 of
+//       a 32-wide k-step; 64 lanes x 16 bytes = one fragment).
 // f32 : v_mfma_f32_32x32x2f32 with the K order inside a 32-wide K tile
 //       permuted so every lane reads 4 consecutive floats per LDS access
 //       (half h of the wave takes k = 16h + 4g + s at step (g, s)); A and B
 //       use the same permutation, so the sum is unchanged.
-// The B fragment is the MFMA's first operand, so each 32x32 accumulator
-// block holds C^T: lane l owns row l%32 of C and columns
-// 8*(r/4) + 4*(l/32) + r%4, r = 0..15 -- four consecutive columns per
-// group of four registers, stored with one vector write.
+// The B fragment is the MFMA's first operand, so each accumulator block
+// holds C^T: a lane owns "quads", four consecutive columns of one row of C,
+// stored with one vector write (16x16 blocks: one quad per lane, row l%16,
+// columns 4*(l/16)..+3; 32x32 blocks: four quads, row l%32, columns
+// 8*q + 4*(l/32)..+3).
 // Fragments of k-step s+1 are read from LDS while the MFMAs of step s run.
 #include "common.h"
 #include "kernels.h"
@@ -88,34 +90,66 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * (CPR * CH) + ((c ^ ((r / RPB) & (CPR - 1))) * CH);
 }
 
-template <typename T, int FM, int FN, int KB>
+// Accumulator layout of a wave's WM x WN sub-tile: AM x AN blocks, QPB
+// quads per lane per block; quad q of block (i, j) is row row(lane, i),
+// columns col(lane, j, q) .. +3 of the sub-tile, values acc[i][j][4q .. 4q+3].
+template <typename T, int WM, int WN>
+struct AccL;
+template <int WM, int WN>
+struct AccL<bf16, WM, WN> {
+  static constexpr int BR = 16, AM = WM / 16, AN = WN / 16, QPB = 1;
+  typedef f32x4 Blk;
+  static __device__ __forceinline__ int row(int lane, int i) { return 16 * i + (lane & 15); }
+  static __device__ __forceinline__ int col(int lane, int j, int q) {
+    return 16 * j + 4 * (lane >> 4);
+  }
+  // sum over the four lanes that hold the columns of one row
+  static __device__ __forceinline__ float row_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+  }
+};
+template <int WM, int WN>
+struct AccL<float, WM, WN> {
+  static constexpr int BR = 32, AM = WM / 32, AN = WN / 32, QPB = 4;
+  typedef f32x16 Blk;
+  static __device__ __forceinline__ int row(int lane, int i) { return 32 * i + (lane & 31); }
+  static __device__ __forceinline__ int col(int lane, int j, int q) {
+    return 32 * j + 8 * q + 4 * (lane >> 5);
+  }
+  static __device__ __forceinline__ float row_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+};
+
+template <typename T, int AM, int AN, int KB>
 struct Frags;
-template <int FM, int FN, int KB>
-struct Frags<bf16, FM, FN, KB> {
-  static constexpr int STEPS = KB / 32;  // 16-wide k-steps per stage
-  bf16x8 a[FM], b[FN];
-  // k-step ks: lane half hf reads chunk 2 ks + hf
+template <int AM, int AN, int KB>
+struct Frags<bf16, AM, AN, KB> {
+  static constexpr int STEPS = KB / 64;  // 32-wide k-steps per stage
+  typedef f32x4 Blk;
+  bf16x8 a[AM], b[AN];
+  // k-step ks: lane quarter q (= lane / 16) reads chunk 4 ks + q of its row
   __device__ __forceinline__ void load(const bf16* As, const bf16* Bs, int arow0,
                                        int brow0, int lane, int ks) {
-    const int r = lane & 31, c = 2 * ks + (lane >> 5);
+    const int r = lane & 15, c = 4 * ks + (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16, KB>(arow0 + i * 32 + r, c));
+    for (int i = 0; i < AM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16, KB>(arow0 + i * 16 + r, c));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16, KB>(brow0 + j * 32 + r, c));
+    for (int j = 0; j < AN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16, KB>(brow0 + j * 16 + r, c));
   }
-  __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
+  __device__ __forceinline__ void mma(f32x4 (&acc)[AM][AN]) const {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < AM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < AN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   }
 };
 template <int FM, int FN, int KB>
 struct Frags<float, FM, FN, KB> {
   static constexpr int STEPS = KB / 32;  // groups of 4 k per lane half
+  typedef f32x16 Blk;
   f32x4 a[FM], b[FN];
   // group g: lane half hf reads chunk hf * STEPS + g
   __device__ __forceinline__ void load(const float* As, const float* Bs, int arow0,
@@ -142,8 +176,8 @@ struct Frags<float, FM, FN, KB> {
 // All MFMAs of one stage, the next step's fragments read while the current
 // step's MFMAs run.
 template <typename T, int FM, int FN, int KB>
-__device__ __forceinline__ void compute_tile(f32x16 (&acc)[FM][FN], const T* As,
-                                             const T* Bs, int arow0, int brow0,
+__device__ __forceinline__ void compute_tile(typename Frags<T, FM, FN, KB>::Blk (&acc)[FM][FN],
+                                             const T* As, const T* Bs, int arow0, int brow0,
                                              int lane) {
   using F = Frags<T, FM, FN, KB>;
   constexpr int NSTEP = F::STEPS;
@@ -233,29 +267,28 @@ __device__ __forceinline__ void load4<float>(const float* p, float* v) {
   v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
 }
 
-// Q/K/V(/gate) epilogue.  A wave owns WM rows (tokens) x FN*32 columns; its
-// columns hold whole heads.  Lane l holds token row l%32 of each 32-row
-// block and, per head, half of that row's HD columns (the other half is in
-// lane l^32).  Per head: optional RMSNorm over the head (sum of squares in
-// the lane plus one exchange with lane l^32), rotary on the pairs
+// Q/K/V(/gate) epilogue.  A wave owns WM rows (tokens) x WN columns; its
+// columns hold whole heads.  A lane holds quads (four consecutive columns)
+// of its rows; per head: optional RMSNorm over the head (sum of squares in
+// the lane, then across the lanes that share the row), rotary on the pairs
 // (d, d + HD/2), which sit in the same lane and register, then the head is
 // staged through this wave's slice of LDS so that the global stores are
 // 16 bytes and coalesced: q/k rows [token][d] go to [b, head, s, :], v goes
 // transposed to V^T [b, head, d, s] (keys contiguous, the layout the
 // attention kernel's P.V product reads).
-template <typename T, int HD, int FM, int FN, int WM>
-__device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
-                                             const GemmParams& p, int row0,
+template <typename T, int HD, int WM, int WN, typename ACC>
+__device__ __forceinline__ void qkv_epilogue(ACC& acc, const GemmParams& p, int row0,
                                              int col0, int lane, T* lds) {
-  constexpr int HB = HD / 32;       // 32-wide blocks per head
+  using L = AccL<T, WM, WN>;
+  constexpr int AM = L::AM, AN = L::AN, QPB = L::QPB;
+  constexpr int HB = HD / L::BR;    // accumulator blocks per head
   constexpr int CH = 16 / sizeof(T);
   constexpr int QLD = HD + CH;      // staged q/k row   [WM][QLD]
   constexpr int VLD = WM + CH;      // staged v^T row   [HD][VLD]
-  static_assert(FN % HB == 0, "wave columns must hold whole heads");
-  const int cl = lane & 31, hi4 = (lane >> 5) * 4;
+  static_assert(AN % HB == 0, "wave columns must hold whole heads");
   const int Sp = (p.S + 63) & ~63;  // V^T rows are padded to 64 keys
 #pragma unroll
-  for (int hh = 0; hh < FN / HB; ++hh) {
+  for (int hh = 0; hh < AN / HB; ++hh) {
     const int c0 = col0 + hh * HD;
     if (c0 >= p.N) continue;
     int seg = 0;
@@ -263,18 +296,20 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
     const int start = seg ? p.seg_end[seg - 1] : 0;
     if (seg == 3) {  // gate columns: sigmoid, float32 [M, G]
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int row = row0 + fm * 32 + cl;
+      for (int i = 0; i < AM; ++i) {
+        const int row = row0 + L::row(lane, i);
         if (row >= p.M) continue;
 #pragma unroll
-        for (int fb = 0; fb < HB; ++fb)
+        for (int jb = 0; jb < HB; ++jb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int col = c0 + fb * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-            if (col < p.N)
-              p.gate[(int64_t)row * p.G + (col - start)] =
-                  1.0f / (1.0f + expf(-acc[fm][hh * HB + fb][r]));
-          }
+          for (int q = 0; q < QPB; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int col = c0 + L::col(lane, jb, q) + e;
+              if (col < p.N)
+                p.gate[(int64_t)row * p.G + (col - start)] =
+                    1.0f / (1.0f + expf(-acc[i][hh * HB + jb][4 * q + e]));
+            }
       }
       continue;
     }
@@ -289,30 +324,31 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
       const bool do_norm = p.qk_norm != 0, do_rope = p.use_rope != 0;
       const T* gw = (const T*)(seg == 0 ? p.q_norm_w : p.k_norm_w);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
+      for (int i = 0; i < AM; ++i) {
         float inv = 1.0f;
         if (do_norm) {
           float ss = 0.f;
 #pragma unroll
-          for (int fb = 0; fb < HB; ++fb)
+          for (int jb = 0; jb < HB; ++jb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float v = acc[fm][hh * HB + fb][r];
+            for (int r = 0; r < 4 * QPB; ++r) {
+              const float v = acc[i][hh * HB + jb][r];
               ss += v * v;
             }
-          ss += __shfl_xor(ss, 32, 64);
+          ss = L::row_sum(ss);
           inv = 1.0f / sqrtf(ss * (1.0f / HD) + p.eps);
         }
-        const int row = row0 + fm * 32 + cl;
+        const int lr = L::row(lane, i);
+        const int row = row0 + lr;
         const int pos = (row < p.M) ? row % p.S : 0;
         const float* cr = p.rope_cos + (int64_t)pos * (HD / 2);
         const float* sr = p.rope_sin + (int64_t)pos * (HD / 2);
-        T* srow = lds + (fm * 32 + cl) * QLD;
+        T* srow = lds + lr * QLD;
 #pragma unroll
-        for (int fb = 0; fb < HB / 2; ++fb)
+        for (int jb = 0; jb < HB / 2; ++jb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = fb * 32 + i * 8 + hi4;  // low member of the pairs
+          for (int q = 0; q < QPB; ++q) {
+            const int d = L::col(lane, jb, q);  // low member of the pairs
             float glo[4] = {1.f, 1.f, 1.f, 1.f}, ghi[4] = {1.f, 1.f, 1.f, 1.f};
             if (do_norm) {
               load4(gw + d, glo);
@@ -325,11 +361,11 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
             }
             float olo[4], ohi[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float lo = glo[j] * (acc[fm][hh * HB + fb][i * 4 + j] * inv);
-              const float hi = ghi[j] * (acc[fm][hh * HB + fb + HB / 2][i * 4 + j] * inv);
-              olo[j] = do_rope ? lo * c[j] - hi * sn[j] : lo;
-              ohi[j] = do_rope ? hi * c[j] + lo * sn[j] : hi;
+            for (int e = 0; e < 4; ++e) {
+              const float lo = glo[e] * (acc[i][hh * HB + jb][4 * q + e] * inv);
+              const float hi = ghi[e] * (acc[i][hh * HB + jb + HB / 2][4 * q + e] * inv);
+              olo[e] = do_rope ? lo * c[e] - hi * sn[e] : lo;
+              ohi[e] = do_rope ? hi * c[e] + lo * sn[e] : hi;
             }
             store4(srow + d, olo[0], olo[1], olo[2], olo[3]);
             store4(srow + d + HD / 2, ohi[0], ohi[1], ohi[2], ohi[3]);
@@ -357,14 +393,16 @@ __device__ __forceinline__ void qkv_epilogue(f32x16 (&acc)[FM][FN],
     } else {
       // stage transposed [d][row], then store key-contiguous runs of V^T
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int i = 0; i < AM; ++i)
 #pragma unroll
-        for (int fb = 0; fb < HB; ++fb)
+        for (int jb = 0; jb < HB; ++jb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int d = fb * 32 + (r >> 2) * 8 + hi4 + (r & 3);
-            lds[d * VLD + fm * 32 + cl] = from_f32<T>(acc[fm][hh * HB + fb][r]);
-          }
+          for (int q = 0; q < QPB; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int d = L::col(lane, jb, q) + e;
+              lds[d * VLD + L::row(lane, i)] = from_f32<T>(acc[i][hh * HB + jb][4 * q + e]);
+            }
       wave_lds_sync();
       // bf16: within each aligned group of 16 keys the row holds keys
       // 0-3, 8-11, 4-7, 12-15 (position and key differ by a swap of bits
@@ -534,13 +572,15 @@ gemm_kernel(const GemmParams p) {
                     kt * BK + b_k[i] < p.K ? b_off[i] + ko : 0xffffffffu);
   };
 
-  f32x16 acc[FM][FN];
+  using L = AccL<T, WM, WN>;
+  constexpr int AM = L::AM, AN = L::AN, QPB = L::QPB;
+  typename L::Blk acc[AM][AN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < AM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < AN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4 * QPB; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (p.K + BK - 1) / BK;
 #pragma unroll
@@ -557,48 +597,48 @@ gemm_kernel(const GemmParams p) {
       wait_vmcnt<0>();
     __syncthreads();
     if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-    compute_tile<T, FM, FN, KB>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
+    compute_tile<T, AM, AN, KB>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
   }
   __syncthreads();  // LDS is free for the epilogue
 
-  // ---- epilogue
-  const int cl = lane & 31, hi4 = (lane >> 5) * 4;
+  // ---- epilogue: each lane stores its quads (four consecutive columns)
   const int lrow0 = mt * BM + wm * WM;  // tile-local (group-local) row base
   if constexpr (EPI == EPI_QKV) {
     // each wave stages its heads in its own slice of the (now idle) LDS
     T* slice = smem + wave * SLICE;
-    qkv_epilogue<T, HDQ, FM, FN, WM>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
+    qkv_epilogue<T, HDQ, WM, WN>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
     return;
   } else if constexpr (PAIRED) {
+    // gate columns are the first half of the wave's columns, up the second
     const int ncol0 = nt * (BN / 2) + wn * (WN / 2);
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int lr = lrow0 + fm * 32 + cl;
+    for (int i = 0; i < AM; ++i) {
+      const int lr = lrow0 + L::row(lane, i);
       if (lr >= row_count) continue;
       T* orow = (T*)p.out + (int64_t)(row_begin + lr) * p.ldo;
 #pragma unroll
-      for (int fn = 0; fn < FN / 2; ++fn)
+      for (int j = 0; j < AN / 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = ncol0 + fn * 32 + i * 8 + hi4;
+        for (int q = 0; q < QPB; ++q) {
+          const int col = ncol0 + L::col(lane, j, q);
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            v[j] = silu_f(acc[fm][fn][i * 4 + j]) * acc[fm][fn + FN / 2][i * 4 + j];
+          for (int e = 0; e < 4; ++e)
+            v[e] = silu_f(acc[i][j][4 * q + e]) * acc[i][j + AN / 2][4 * q + e];
           if (col + 3 < p.N) {
             store4(orow + col, v[0], v[1], v[2], v[3]);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (col + j < p.N) orow[col + j] = from_f32<T>(v[j]);
+            for (int e = 0; e < 4; ++e)
+              if (col + e < p.N) orow[col + e] = from_f32<T>(v[e]);
           }
         }
     }
     return;
   } else {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int lr = lrow0 + fm * 32 + cl;
+    for (int i = 0; i < AM; ++i) {
+      const int lr = lrow0 + L::row(lane, i);
       if (lr >= row_count) continue;
       const int64_t row = row_begin + lr;
       int64_t orow = row * p.ldo;
@@ -609,14 +649,14 @@ gemm_kernel(const GemmParams p) {
         wrow = p.pair_weight[pair];
       }
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int j = 0; j < AN; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = nt * BN + wn * WN + fn * 32 + i * 8 + hi4;
+        for (int q = 0; q < QPB; ++q) {
+          const int col = nt * BN + wn * WN + L::col(lane, j, q);
           if (col >= p.N) continue;
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = acc[fm][fn][i * 4 + j];
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
           const int64_t o = orow + col;
           const bool full = col + 3 < p.N;
           if constexpr (EPI == EPI_STORE) {
@@ -624,9 +664,9 @@ gemm_kernel(const GemmParams p) {
               if (p.out_f32) store4((float*)p.out + o, v[0], v[1], v[2], v[3]);
               else store4((T*)p.out + o, v[0], v[1], v[2], v[3]);
             } else {
-              for (int j = 0; j < 4 && col + j < p.N; ++j) {
-                if (p.out_f32) ((float*)p.out)[o + j] = v[j];
-                else ((T*)p.out)[o + j] = from_f32<T>(v[j]);
+              for (int e = 0; e < 4 && col + e < p.N; ++e) {
+                if (p.out_f32) ((float*)p.out)[o + e] = v[e];
+                else ((T*)p.out)[o + e] = from_f32<T>(v[e]);
               }
             }
           } else if constexpr (EPI == EPI_RESID) {
@@ -635,42 +675,42 @@ gemm_kernel(const GemmParams p) {
               if (p.resid_f32) load4((const float*)p.resid + o, res);
               else load4((const T*)p.resid + o, res);
             } else {
-              for (int j = 0; j < 4; ++j)
-                res[j] = (col + j < p.N) ? (p.resid_f32 ? ((const float*)p.resid)[o + j]
-                                                        : to_f32(((const T*)p.resid)[o + j]))
+              for (int e = 0; e < 4; ++e)
+                res[e] = (col + e < p.N) ? (p.resid_f32 ? ((const float*)p.resid)[o + e]
+                                                        : to_f32(((const T*)p.resid)[o + e]))
                                          : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sum[j] = res[j] + v[j];
+            for (int e = 0; e < 4; ++e) sum[e] = res[e] + v[e];
             if (full) {
               if (p.out_f32p) store4(p.out_f32p + o, sum[0], sum[1], sum[2], sum[3]);
               if (p.out_model) store4((T*)p.out_model + o, sum[0], sum[1], sum[2], sum[3]);
               if (p.out_raw) store4(p.out_raw + o, v[0], v[1], v[2], v[3]);
             } else {
-              for (int j = 0; j < 4 && col + j < p.N; ++j) {
-                if (p.out_f32p) p.out_f32p[o + j] = sum[j];
-                if (p.out_model) ((T*)p.out_model)[o + j] = from_f32<T>(sum[j]);
-                if (p.out_raw) p.out_raw[o + j] = v[j];
+              for (int e = 0; e < 4 && col + e < p.N; ++e) {
+                if (p.out_f32p) p.out_f32p[o + e] = sum[e];
+                if (p.out_model) ((T*)p.out_model)[o + e] = from_f32<T>(sum[e]);
+                if (p.out_raw) p.out_raw[o + e] = v[e];
               }
             }
           } else {
             float w[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int e = 0; e < 4; ++e) {
               if constexpr (EPI == EPI_RELU2) {
-                const float rl = fmaxf(v[j], 0.f);
-                w[j] = rl * rl;
+                const float rl = fmaxf(v[e], 0.f);
+                w[e] = rl * rl;
               } else if constexpr (EPI == EPI_XIELU) {
-                w[j] = xielu_f(v[j], p.xa_p, p.xa_n, p.xbeta, p.xeps);
+                w[e] = xielu_f(v[e], p.xa_p, p.xa_n, p.xbeta, p.xeps);
               } else {  // EPI_MOE_DOWN
-                w[j] = wrow * v[j];
+                w[e] = wrow * v[e];
               }
             }
             if (full) {
               store4((T*)p.out + o, w[0], w[1], w[2], w[3]);
             } else {
-              for (int j = 0; j < 4 && col + j < p.N; ++j)
-                ((T*)p.out)[o + j] = from_f32<T>(w[j]);
+              for (int e = 0; e < 4 && col + e < p.N; ++e)
+                ((T*)p.out)[o + e] = from_f32<T>(w[e]);
             }
           }
         }
