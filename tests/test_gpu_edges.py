@@ -1,0 +1,204 @@
+"""GPU parity on the degenerate and boundary cases of the block, through the
+C ABI, against the fp64 oracle (bars as in test_gpu_parity.py):
+
+  * one token per sequence, and lengths that are not multiples of the 8-
+    and 16-key groups of the transposed value store;
+  * hidden and MLP widths that are multiples of 8 but not of any tile
+    (ragged K and N edges in every GEMM);
+  * attention masks with left padding and holes, including query rows that
+    see no key at all (their attention output is 0);
+  * a window of one key (each query sees itself only) and a window longer
+    than the sequence (identical to full causal);
+  * exact ties among the router's biased scores (the lower expert index
+    wins, slots in descending score order);
+  * the widest hidden size the library accepts (8192) and the largest
+    expert count (256).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import block as ob
+from transformer_decoder_block_amd import synth
+from tests import bf16_emulation as em
+from tests.blockrun import Run, dev, rel_err
+from tests.test_gpu_parity import BF16_BAR, F32_BAR, check_scores, floor_bar, near_tie
+
+pytestmark = pytest.mark.gpu
+
+TAPS = ["layer_input", "attention_norm_output", "attention_scores", "layer_mid",
+        "mlp_input", "layer_output", "attention_output", "mlp_output"]
+MOE_TAPS = ["router_logits", "expert_indices", "expert_weights"]
+
+
+def llama(name, dtype, B, S, H=256, nh=4, nkv=2, hd=64, I=344, **kw):
+    return synth.Workload(name, dtype, B=B, S=S, H=H, nh=nh, nkv=nkv, hd=hd,
+                          mlp="swiglu", I=I, seed=kw.pop("seed", 40), **kw)
+
+
+def afmoe(name, dtype, B, S, E=8, top_k=2, **kw):
+    base = dict(H=256, nh=4, nkv=2, hd=64, mlp="moe", qk_norm=True, sandwich=True,
+                window=32, head_gate=4, E=E, top_k=top_k, I_e=96, n_shared=1,
+                route_scale=2.826, seed=41)
+    base.update(kw)
+    return synth.Workload(name, dtype, B=B, S=S, **base)
+
+
+def taps_for(w):
+    return TAPS + (MOE_TAPS if w.mlp == "moe" else [])
+
+
+def check_f32(run, mask=None):
+    """End to end from layer_input, every tap, at the float32 bar."""
+    w = run.w
+    md = None if mask is None else torch.from_numpy(mask).cuda()
+    out = run.forward(taps_for(w), mask=md)
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    for b in range(w.B):
+        mk = None if mask is None else mask[b]
+        r = ob.block_forward(x64[b], mk, W, cfg)
+        keep = np.ones(w.S, bool)
+        if w.mlp == "moe":
+            gi = np.sort(out["expert_indices"][b], -1)
+            diff = np.any(gi != np.sort(r["expert_indices"], -1), -1)
+            assert np.all(near_tie(r["router_logits"], W["expert_bias"], w.top_k)[diff])
+            keep = ~diff
+        for name in ("attention_norm_output", "layer_mid", "mlp_input", "attention_output"):
+            assert rel_err(out[name][b], r[name]) <= F32_BAR, (name, b)
+        for name in ("mlp_output", "layer_output"):
+            assert rel_err(out[name][b][keep], r[name][keep]) <= F32_BAR, (name, b)
+        check_scores(out["attention_scores"][b], r["attention_scores"], F32_BAR)
+    return out
+
+
+def check_bf16(run, mask=None):
+    """Stagewise, each stage fed the GPU's own tap of its input."""
+    w = run.w
+    md = None if mask is None else torch.from_numpy(mask).cuda()
+    out = run.forward(taps_for(w), mask=md)
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    lo = torch.from_numpy(out["layer_output"].astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(lo.view(torch.int16), out["y_raw"].cpu().view(torch.int16))
+    for b in range(w.B):
+        mk = None if mask is None else mask[b]
+        a_tap = out["attention_norm_output"][b]
+        assert rel_err(a_tap, ob.rms_norm(x64[b], W["w_in_norm"], w.eps)) <= BF16_BAR
+        att = ob.attention_sublayer(x64[b], a_tap, mk, W, cfg)
+        check_scores(out["attention_scores"][b], att["attention_scores"], BF16_BAR)
+        assert rel_err(out["layer_mid"][b], att["layer_mid"]) <= BF16_BAR
+        fl = rel_err(em.attention_sublayer_bf16(x64[b], a_tap, mk, W, cfg)["attention_output"],
+                     att["attention_output"])
+        assert rel_err(out["attention_output"][b], att["attention_output"]) <= floor_bar(fl)
+        mid_tap, m_tap = out["layer_mid"][b], out["mlp_input"][b]
+        assert rel_err(m_tap, ob.mlp_norm(mid_tap, W, cfg)) <= BF16_BAR
+        logits = None
+        if w.mlp == "moe":
+            logits = out["router_logits"][b]
+            _, idx, wts = ob.route(logits, W["expert_bias"], w.top_k, w.route_scale, "bf16")
+            assert np.array_equal(out["expert_indices"][b], idx)
+            np.testing.assert_allclose(out["expert_weights"][b], wts, rtol=2e-6, atol=1e-7)
+        mo = ob.mlp_sublayer(mid_tap, m_tap, W, cfg, router_logits=logits)
+        assert rel_err(out["layer_output"][b], mo["layer_output"]) <= BF16_BAR
+    return out
+
+
+CHECK = {"f32": check_f32, "bf16": check_bf16}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("S", [1, 7, 13, 72])
+def test_short_and_ragged_sequences(dtype, S):
+    CHECK[dtype](Run(llama(f"llama_s{S}", dtype, B=2, S=S)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_moe(dtype):
+    CHECK[dtype](Run(afmoe("afmoe_s1", dtype, B=3, S=1)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_widths(dtype):
+    # hidden 264 and MLP width 200: K and N tails in every GEMM and the norms
+    CHECK[dtype](Run(llama("llama_ragged", dtype, B=2, S=45, H=264, I=200)))
+
+
+def holes_mask(B, S, seed=7):
+    """Sequence 0: about a fifth of the keys masked at random; sequence 1:
+    the first 9 tokens masked (left padding: query rows 0..8 see no key)."""
+    rng = np.random.default_rng(seed)
+    m = np.ones((B, S), np.int32)
+    m[0] = (rng.random(S) > 0.2).astype(np.int32)
+    m[1, :9] = 0
+    return m
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("family", ["llama", "afmoe"])
+def test_left_padding_and_holes(dtype, family):
+    S = 150
+    w = llama("llama_holes", dtype, B=2, S=S) if family == "llama" else \
+        afmoe("afmoe_holes", dtype, B=2, S=S)
+    run = Run(w)
+    mask = holes_mask(2, S)
+    out = CHECK[dtype](run, mask)
+    # query rows that see no key: no attention output at all
+    assert np.all(out["attention_output"][1, :9] == 0.0)
+    assert np.all(np.isneginf(out["attention_scores"][1, :, :9]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_window_of_one(dtype):
+    w = llama("llama_w1", dtype, B=2, S=100, window=1)
+    CHECK[dtype](Run(w))
+
+
+def test_window_longer_than_sequence_is_causal():
+    w = llama("llama_wlong", "bf16", B=2, S=130)
+    causal = Run(w).forward(["layer_output"])
+    longw = Run(w.replace(window=1000)).forward(["layer_output"])
+    assert np.array_equal(causal["y"], longw["y"])
+    assert np.array_equal(causal["layer_output"], longw["layer_output"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_exact_ties(dtype):
+    """Experts 0-3 share one router row and one bias, as do 4-5: their
+    biased scores tie exactly for every token."""
+    w = afmoe("afmoe_ties", dtype, B=2, S=64, E=8, top_k=3)
+    run = Run(w)
+    for grp in ((0, 1, 2, 3), (4, 5)):
+        for e in grp[1:]:
+            run.Wst["w_router"][e] = run.Wst["w_router"][grp[0]]
+            run.Wst["expert_bias"][e] = run.Wst["expert_bias"][grp[0]]
+    # same device buffers (the handle keeps their addresses), new contents
+    run.Wd["w_router"].copy_(dev(run.Wst["w_router"], w.dtype))
+    run.Wd["expert_bias"].copy_(dev(run.Wst["expert_bias"], "f32"))
+    run._W64 = None
+    out = run.forward(["router_logits", "expert_indices", "expert_weights"])
+    W = run.W64
+    for b in range(w.B):
+        lg = out["router_logits"][b]
+        assert np.array_equal(lg[:, 0], lg[:, 3]) and np.array_equal(lg[:, 4], lg[:, 5])
+        _, idx, wts = ob.route(lg, W["expert_bias"], w.top_k, w.route_scale, w.dtype)
+        assert np.array_equal(out["expert_indices"][b], idx)
+        np.testing.assert_allclose(out["expert_weights"][b], wts, rtol=2e-6, atol=1e-7)
+        # a tied group is taken lowest index first, in consecutive slots
+        for t in range(w.S):
+            sel = list(idx[t])
+            for grp in ((0, 1, 2, 3), (4, 5)):
+                got = [e for e in sel if e in grp]
+                assert got == sorted(got)
+                assert got == list(grp[:len(got)])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_widest_hidden(dtype):
+    w = llama("llama_h8192", dtype, B=1, S=40, H=8192, nh=64, nkv=8, hd=128, I=256)
+    CHECK[dtype](Run(w))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_most_experts(dtype):
+    w = afmoe("afmoe_e256", dtype, B=1, S=96, E=256, top_k=8, I_e=32, window=0,
+              head_gate=0)
+    CHECK[dtype](Run(w))
