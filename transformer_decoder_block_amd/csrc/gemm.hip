@@ -560,16 +560,25 @@ gemm_kernel(const GemmParams p) {
     b_off[i] = ok ? (uint32_t)(((int64_t)n * p.ldb + kch * CH) * sizeof(T))
                   : p.b_bytes[seg];
   }
+  // The k of this lane's chunk is the same in every load instruction (the
+  // swizzle repeats every NW*RPI rows), so one K-tail test covers a stage.
+  static_assert((TL::NW * RPI / RPB) % CPR == 0, "swizzle period divides the load stride");
+  const int k_lane = a_k[0];
+  // Dense A rows without a gather: offsets are base + i * stride (rows past
+  // M read whatever the resource holds or zeros, and are never stored).
+  const bool a_dense = !GROUPED && p.a_gather == nullptr;
+  const uint32_t a_stride = (uint32_t)((int64_t)TL::NW * RPI * p.lda * sizeof(T));
   auto issue = [&](int kt, int buf) {
     const uint32_t ko = kt * BK * sizeof(T);
+    const bool kin = kt * BK + k_lane < p.K;
 #pragma unroll
     for (int i = 0; i < AL; ++i)
       load16_to_lds(rA, As(buf) + (TL::NW * i + wave) * RPI * LD,
-                    kt * BK + a_k[i] < p.K ? a_off[i] + ko : p.a_bytes);
+                    !kin ? p.a_bytes : (a_dense ? a_off[0] + i * a_stride : a_off[i]) + ko);
 #pragma unroll
     for (int i = 0; i < BL; ++i)
       load16_to_lds(rB[i], Bs(buf) + (TL::NW * i + wave) * RPI * LD,
-                    kt * BK + b_k[i] < p.K ? b_off[i] + ko : 0xffffffffu);
+                    kin ? b_off[i] + ko : 0xffffffffu);
   };
 
   using L = AccL<T, WM, WN>;
