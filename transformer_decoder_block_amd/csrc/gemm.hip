@@ -463,8 +463,10 @@ gemm_kernel(const GemmParams p) {
   constexpr int SLICE = (WM * (128 + CHT) > 128 * (WM + CHT)) ? WM * (128 + CHT)
                                                                : 128 * (WM + CHT);
   constexpr int MAIN = NS * (BM + BN) * LD;
-  constexpr int SMEM = (EPI == EPI_QKV && TL::NW * SLICE > MAIN) ? TL::NW * SLICE : MAIN;
-  __shared__ __attribute__((aligned(16))) T smem[SMEM];
+  constexpr int SMEM0 = (EPI == EPI_QKV && TL::NW * SLICE > MAIN) ? TL::NW * SLICE : MAIN;
+  // grouped: 257 ints of tile prefix sums after the operand tiles
+  constexpr int SMEM = GROUPED ? SMEM0 + 257 * 4 / (int)sizeof(T) + 4 : SMEM0;
+  __shared__ __attribute__((aligned(1024))) T smem[SMEM];
   auto As = [&](int b) { return smem + b * (BM * LD); };
   auto Bs = [&](int b) { return smem + NS * BM * LD + b * (BN * LD); };
 
@@ -481,19 +483,46 @@ gemm_kernel(const GemmParams p) {
     // XCD) are the N tiles of one M tile, so the gathered A rows are read
     // once and an expert's weights are shared by its M tiles in that L2
     const int id = xcd_contiguous(blockIdx.x, gridDim.x);
-    int t = id / num_n;
+    const int t = id / num_n;
     nt = id % num_n;
-    int g = 0;
-    for (; g < p.ngroups; ++g) {
-      const int tiles = (p.gcnt[g] + BM - 1) / BM;
-      if (t < tiles) break;
-      t -= tiles;
+    // M tiles per group, exclusive prefix sums in LDS (the first wave: lane
+    // j owns groups 4j .. 4j+3, at most 256 groups); the group of tile t is
+    // then found by a binary search
+    int* tpre = reinterpret_cast<int*>(smem + SMEM0);
+    if (wave == 0) {
+      int c[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = 4 * lane + q;
+        c[q] = g < p.ngroups ? (p.gcnt[g] + BM - 1) / BM : 0;
+        sum += c[q];
+      }
+      int inc = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+      }
+      int ex = inc - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        tpre[4 * lane + q] = ex;
+        ex += c[q];
+      }
+      if (lane == 63) tpre[256] = inc;
     }
-    if (g >= p.ngroups) return;  // idle tile of the worst-case grid
-    group = g;
-    mt = t;
-    row_begin = p.goff[g];
-    row_count = p.gcnt[g];
+    __syncthreads();
+    if (t >= tpre[256]) return;  // idle tile of the worst-case grid
+    int lo = 0, hi = p.ngroups;  // tpre[lo] <= t < tpre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tpre[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    group = lo;
+    mt = t - tpre[lo];
+    row_begin = p.goff[lo];
+    row_count = p.gcnt[lo];
   } else {
     const int num_m = (p.M + BM - 1) / BM;
     const int id = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -750,6 +779,7 @@ static hipError_t launch(const GemmParams& p, int max_rows, hipStream_t s) {
 using TileL = Tile<bf16, 256, 256, 2, 4, 128, 2>;
 using TileQ = Tile<bf16, 256, 256, 4, 2, 128, 2>;  // 64x128 wave tiles: whole heads per wave
 using TileS = Tile<bf16, 128, 128, 4, 1, 128, 2>;
+using TileR = Tile<bf16, 64, 64, 2, 2, 128, 2>;    // narrow outputs (the router)
 using TileF = Tile<float, 128, 128, 4, 1, 128, 2>;
 
 template <typename T, class TL>
@@ -769,7 +799,7 @@ static hipError_t dispatch_epi(EpiKind epi, bool grouped, const GemmParams& p,
     case EPI_RELU2: return launch<T, TL, EPI_RELU2, false>(p, max_rows, s);
     case EPI_XIELU: return launch<T, TL, EPI_XIELU, false>(p, max_rows, s);
     case EPI_QKV:
-      if constexpr (TL::FM <= 2) {
+      if constexpr (TL::FM <= 2 && TL::WN >= 128) {
         if (p.hd == 64) return launch<T, TL, EPI_QKV, false, 64>(p, max_rows, s);
         return launch<T, TL, EPI_QKV, false, 128>(p, max_rows, s);
       }
@@ -794,7 +824,10 @@ hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
   }
   const long tiles_l = (long)((max_rows + 255) / 256) * ((p.N + n_per - 1) / n_per);
   if (tiles_l >= 256) return dispatch_epi<bf16, TileL>(epi, grouped, p, max_rows, s);
-  return dispatch_epi<bf16, TileS>(epi, grouped, p, max_rows, s);
+  const long tiles_s = (long)((max_rows + 127) / 128) * ((p.N + n_per / 2 - 1) / (n_per / 2));
+  if (tiles_s >= 256 || grouped || epi != EPI_STORE)
+    return dispatch_epi<bf16, TileS>(epi, grouped, p, max_rows, s);
+  return launch<bf16, TileR, EPI_STORE, false>(p, max_rows, s);
 }
 
 }  // namespace blk
