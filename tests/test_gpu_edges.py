@@ -202,3 +202,22 @@ def test_most_experts(dtype):
     w = afmoe("afmoe_e256", dtype, B=1, S=96, E=256, top_k=8, I_e=32, window=0,
               head_gate=0)
     CHECK[dtype](Run(w))
+
+
+def test_split_tail_tiles():
+    """o_proj at 4352 tokens x 4096 outputs, K = 64 heads x 128 = 8192, is
+    272 tiles of 256 x 256 with 128 K stages on a 256-CU part: its last 16
+    tiles (rows 4096-4351) run as two K halves summed by the fixup.  Their
+    rows of layer_mid match the oracle like any other row, and y is still
+    the rounding of the float32 layer_output."""
+    w = llama("llama_split", "bf16", B=1, S=4352, H=4096, nh=64, nkv=8, hd=128, I=512)
+    run = Run(w)
+    d = run.forward(["attention_norm_output", "layer_mid", "layer_output"], on_device=True)
+    lo = d["layer_output"].to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(lo, d["y_raw"].view(torch.int16))
+    from tests.blockrun import host
+    rows = np.array([0, 1, 2047, 4095, 4096, 4097, 4200, 4350, 4351])
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    a_tap = host(d["attention_norm_output"][0])
+    att = ob.attention_sublayer(x64[0], a_tap, None, W, cfg, rows)
+    assert rel_err(host(d["layer_mid"][0][torch.from_numpy(rows).cuda()]), att["layer_mid"]) <= BF16_BAR

@@ -44,6 +44,7 @@ struct blk_handle {
   // workspace views
   void *a = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *premix = nullptr,
        *m = nullptr, *neur = nullptr, *logits = nullptr, *stage = nullptr, *nsh = nullptr;
+  float* split = nullptr;  // GEMM tail-split partial tiles
   float *gate = nullptr, *o = nullptr, *mid = nullptr, *mlp_raw = nullptr, *ew = nullptr,
         *rope_cos = nullptr, *rope_sin = nullptr;
   int *eidx = nullptr, *gcnt = nullptr, *goff = nullptr, *row_token = nullptr,
@@ -55,6 +56,10 @@ struct blk_handle {
 };
 
 static constexpr int PROF_MARKS = 32;  // marks per forward
+
+// Scratch for the GEMMs' tail split: up to 128 float32 tiles of 256 x 256,
+// two K halves each.
+static constexpr size_t SPLIT_WS_BYTES = (size_t)128 * 2 * 256 * 256 * 4;
 
 // Record a timing mark on the stream: the span from this mark to the next
 // one is charged to `name`.
@@ -198,6 +203,7 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
       add((void**)&h->mlp_raw, T * H * 4);
     }
   }
+  add((void**)&h->split, SPLIT_WS_BYTES);
   if (c.use_rope) {
     add((void**)&h->rope_cos, (size_t)c.max_seq * (hd / 2) * 4);
     add((void**)&h->rope_sin, (size_t)c.max_seq * (hd / 2) * 4);
@@ -378,9 +384,11 @@ blk_status check_weights(const blk_handle* h, const blk_weights* w) {
       return fail(BLK_E_HIP, std::string(what) + ": " + hipGetErrorString(e_));   \
   } while (0)
 
-GemmParams gp0() {
+GemmParams gp0(const blk_handle* h) {
   GemmParams p;
   memset(&p, 0, sizeof(p));
+  p.split_ws = h->split;
+  p.split_ws_bytes = SPLIT_WS_BYTES;
   return p;
 }
 
@@ -430,7 +438,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
 
   // (2) fused Q/K/V(/gate) projection with q/k norm + rotary epilogue
   {
-    GemmParams p = gp0();
+    GemmParams p = gp0(h);
     p.M = T;
     p.K = H;
     p.A = h->a;
@@ -497,7 +505,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
 
   // (4) o_proj (+ residual) and the MLP-input norm
   {
-    GemmParams p = gp0();
+    GemmParams p = gp0(h);
     p.M = T;
     p.N = H;
     p.K = nh * hd;
@@ -540,7 +548,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
   // (5) MLP
   if (!moe) {
     const int I = c.intermediate;
-    GemmParams p = gp0();
+    GemmParams p = gp0(h);
     p.M = T;
     p.N = I;
     p.K = H;
@@ -575,7 +583,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     prof_mark(h, "gemm_up", s);
     HIP_TRY(gemm(dt, epi, p, T, s), "mlp up gemm");
 
-    GemmParams d = gp0();
+    GemmParams d = gp0(h);
     d.M = T;
     d.N = H;
     d.K = I;
@@ -616,7 +624,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
   const int E = c.num_experts, kk = c.top_k, Ie = c.moe_intermediate;
   const int Ish = Ie * c.num_shared_experts;
   {
-    GemmParams p = gp0();  // router.gate: logits in the model dtype
+    GemmParams p = gp0(h);  // router.gate: logits in the model dtype
     p.M = T;
     p.N = E;
     p.K = H;
@@ -651,7 +659,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
                        h->hist, s),
           "dispatch");
   {
-    GemmParams p = gp0();  // routed experts: gate/up + SwiGLU
+    GemmParams p = gp0(h);  // routed experts: gate/up + SwiGLU
     p.M = T * kk;
     p.N = Ie;
     p.K = H;
@@ -675,7 +683,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     HIP_TRY(gemm(dt, EPI_SWIGLU, p, T * kk, s), "expert gate/up gemm");
   }
   {
-    GemmParams p = gp0();  // routed experts: down, scaled by the slot weight
+    GemmParams p = gp0(h);  // routed experts: down, scaled by the slot weight
     p.M = T * kk;
     p.N = H;
     p.K = Ie;
@@ -699,7 +707,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     HIP_TRY(gemm(dt, EPI_MOE_DOWN, p, T * kk, s), "expert down gemm");
   }
   if (Ish > 0) {
-    GemmParams p = gp0();  // shared expert
+    GemmParams p = gp0(h);  // shared expert
     p.M = T;
     p.N = Ish;
     p.K = H;
@@ -716,7 +724,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     p.ldo = Ish;
     prof_mark(h, "gemm_shared_up", s);
     HIP_TRY(gemm(dt, EPI_SWIGLU, p, T, s), "shared gate/up gemm");
-    GemmParams d = gp0();
+    GemmParams d = gp0(h);
     d.M = T;
     d.N = H;
     d.K = Ish;

@@ -73,6 +73,17 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int nblk) {
                      : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Tile id -> (mt, nt): GROUP_M rows of tiles are walked column by column,
+// so the tiles in flight share their A and B panels.
+__device__ __forceinline__ void tile_coords(int id, int num_m, int num_n, int& mt, int& nt) {
+  constexpr int GROUP_M = 8;
+  const int width = GROUP_M * num_n;
+  const int first_m = (id / width) * GROUP_M;
+  const int gsz = min(num_m - first_m, GROUP_M);
+  mt = first_m + (id % width) % gsz;
+  nt = (id % width) / gsz;
+}
+
 // One direct-to-LDS load per lane: 16 bytes at byte offset voff of the
 // buffer land at lds + 16 * lane (lds is the wave's uniform base).
 __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, const void* lds,
@@ -265,6 +276,85 @@ template <>
 __device__ __forceinline__ void load4<float>(const float* p, float* v) {
   const float4 w = *reinterpret_cast<const float4*>(p);
   v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+}
+
+// One quad (four consecutive columns col..col+3 of one output row, values
+// v) through the elementwise epilogue EPI; orow is the row's element offset
+// in the output(s).  Columns at or past N are not written.
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_quad(const GemmParams& p, int64_t orow, int col,
+                                         const float (&v)[4], float wrow) {
+  const int64_t o = orow + col;
+  const bool full = col + 3 < p.N;
+  if constexpr (EPI == EPI_STORE) {
+    if (full) {
+      if (p.out_f32) store4((float*)p.out + o, v[0], v[1], v[2], v[3]);
+      else store4((T*)p.out + o, v[0], v[1], v[2], v[3]);
+    } else {
+      for (int e = 0; e < 4 && col + e < p.N; ++e) {
+        if (p.out_f32) ((float*)p.out)[o + e] = v[e];
+        else ((T*)p.out)[o + e] = from_f32<T>(v[e]);
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    float res[4], sum[4];
+    if (full) {
+      if (p.resid_f32) load4((const float*)p.resid + o, res);
+      else load4((const T*)p.resid + o, res);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        res[e] = (col + e < p.N) ? (p.resid_f32 ? ((const float*)p.resid)[o + e]
+                                                : to_f32(((const T*)p.resid)[o + e]))
+                                 : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum[e] = res[e] + v[e];
+    if (full) {
+      if (p.out_f32p) store4(p.out_f32p + o, sum[0], sum[1], sum[2], sum[3]);
+      if (p.out_model) store4((T*)p.out_model + o, sum[0], sum[1], sum[2], sum[3]);
+      if (p.out_raw) store4(p.out_raw + o, v[0], v[1], v[2], v[3]);
+    } else {
+      for (int e = 0; e < 4 && col + e < p.N; ++e) {
+        if (p.out_f32p) p.out_f32p[o + e] = sum[e];
+        if (p.out_model) ((T*)p.out_model)[o + e] = from_f32<T>(sum[e]);
+        if (p.out_raw) p.out_raw[o + e] = v[e];
+      }
+    }
+  } else {
+    float w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (EPI == EPI_RELU2) {
+        const float rl = fmaxf(v[e], 0.f);
+        w[e] = rl * rl;
+      } else if constexpr (EPI == EPI_XIELU) {
+        w[e] = xielu_f(v[e], p.xa_p, p.xa_n, p.xbeta, p.xeps);
+      } else {  // EPI_MOE_DOWN
+        w[e] = wrow * v[e];
+      }
+    }
+    if (full) {
+      store4((T*)p.out + o, w[0], w[1], w[2], w[3]);
+    } else {
+      for (int e = 0; e < 4 && col + e < p.N; ++e) ((T*)p.out)[o + e] = from_f32<T>(w[e]);
+    }
+  }
+}
+
+// SwiGLU quad: neurons col..col+3 of one row from their gate and up values.
+template <typename T>
+__device__ __forceinline__ void swiglu_quad(const GemmParams& p, T* orow, int col,
+                                            const float (&g)[4], const float (&u)[4]) {
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = silu_f(g[e]) * u[e];
+  if (col + 3 < p.N) {
+    store4(orow + col, v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < p.N) orow[col + e] = from_f32<T>(v[e]);
+  }
 }
 
 // Q/K/V(/gate) epilogue.  A wave owns WM rows (tokens) x WN columns; its
@@ -478,6 +568,7 @@ gemm_kernel(const GemmParams p) {
 
   // ---- which tile
   int mt, nt, row_begin = 0, row_count = p.M, group = 0;
+  int split_slot = -1;  // >= 0: this block computes K half (split_slot & 1) of a tail tile
   if constexpr (GROUPED) {
     // one dimension: consecutive ids (which the renumbering keeps on one
     // XCD) are the N tiles of one M tile, so the gathered A rows are read
@@ -525,13 +616,18 @@ gemm_kernel(const GemmParams p) {
     row_count = p.gcnt[lo];
   } else {
     const int num_m = (p.M + BM - 1) / BM;
-    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
-    constexpr int GROUP_M = 8;
-    const int width = GROUP_M * num_n;
-    const int first_m = (id / width) * GROUP_M;
-    const int gsz = min(num_m - first_m, GROUP_M);
-    mt = first_m + (id % width) % gsz;
-    nt = (id % width) / gsz;
+    // blocks [0, F) are whole tiles; with a tail split, blocks F + u are
+    // K half (u & 1) of tile F + u / 2 (dispatched last, spread over XCDs)
+    const int F = num_m * num_n - p.split_tiles;
+    int id;
+    if (p.split_tiles > 0 && (int)blockIdx.x >= F) {
+      const int u = blockIdx.x - F;
+      id = F + u / 2;
+      split_slot = u;
+    } else {
+      id = xcd_contiguous(blockIdx.x, p.split_tiles > 0 ? F : gridDim.x);
+    }
+    tile_coords(id, num_m, num_n, mt, nt);
   }
 
   // ---- direct-to-LDS loads.  Load instruction i of wave w fills tile rows
@@ -620,10 +716,12 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 4 * QPB; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (p.K + BK - 1) / BK;
+  const int nk_all = (p.K + BK - 1) / BK;
+  const int k0 = split_slot >= 0 && (split_slot & 1) ? nk_all / 2 : 0;
+  const int nk = split_slot >= 0 ? ((split_slot & 1) ? nk_all - nk_all / 2 : nk_all / 2) : nk_all;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(st, st);
+    if (st < nk) issue(k0 + st, st);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt % NS;
     // this thread's loads of stage kt have landed (the loads of the later
@@ -634,10 +732,28 @@ gemm_kernel(const GemmParams p) {
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    if (kt + NS - 1 < nk) issue(k0 + kt + NS - 1, (kt + NS - 1) % NS);
     compute_tile<T, AM, AN, KB>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
   }
   __syncthreads();  // LDS is free for the epilogue
+
+  if constexpr (!GROUPED && EPI != EPI_QKV) {
+    if (split_slot >= 0) {
+      // raw float32 partial tile [BM][BN] (tile-local), finished by the fixup
+      float* ws = p.split_ws + (size_t)split_slot * BM * BN;
+#pragma unroll
+      for (int i = 0; i < AM; ++i)
+#pragma unroll
+        for (int j = 0; j < AN; ++j)
+#pragma unroll
+          for (int q = 0; q < QPB; ++q) {
+            const int r = wm * WM + L::row(lane, i), c = wn * WN + L::col(lane, j, q);
+            store4(ws + r * BN + c, acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                   acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+      return;
+    }
+  }
 
   // ---- epilogue: each lane stores its quads (four consecutive columns)
   const int lrow0 = mt * BM + wm * WM;  // tile-local (group-local) row base
@@ -658,18 +774,13 @@ gemm_kernel(const GemmParams p) {
       for (int j = 0; j < AN / 2; ++j)
 #pragma unroll
         for (int q = 0; q < QPB; ++q) {
-          const int col = ncol0 + L::col(lane, j, q);
-          float v[4];
+          float g[4], u[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = silu_f(acc[i][j][4 * q + e]) * acc[i][j + AN / 2][4 * q + e];
-          if (col + 3 < p.N) {
-            store4(orow + col, v[0], v[1], v[2], v[3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (col + e < p.N) orow[col + e] = from_f32<T>(v[e]);
+          for (int e = 0; e < 4; ++e) {
+            g[e] = acc[i][j][4 * q + e];
+            u[e] = acc[i][j + AN / 2][4 * q + e];
           }
+          swiglu_quad<T>(p, orow, ncol0 + L::col(lane, j, q), g, u);
         }
     }
     return;
@@ -695,81 +806,100 @@ gemm_kernel(const GemmParams p) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          const int64_t o = orow + col;
-          const bool full = col + 3 < p.N;
-          if constexpr (EPI == EPI_STORE) {
-            if (full) {
-              if (p.out_f32) store4((float*)p.out + o, v[0], v[1], v[2], v[3]);
-              else store4((T*)p.out + o, v[0], v[1], v[2], v[3]);
-            } else {
-              for (int e = 0; e < 4 && col + e < p.N; ++e) {
-                if (p.out_f32) ((float*)p.out)[o + e] = v[e];
-                else ((T*)p.out)[o + e] = from_f32<T>(v[e]);
-              }
-            }
-          } else if constexpr (EPI == EPI_RESID) {
-            float res[4], sum[4];
-            if (full) {
-              if (p.resid_f32) load4((const float*)p.resid + o, res);
-              else load4((const T*)p.resid + o, res);
-            } else {
-              for (int e = 0; e < 4; ++e)
-                res[e] = (col + e < p.N) ? (p.resid_f32 ? ((const float*)p.resid)[o + e]
-                                                        : to_f32(((const T*)p.resid)[o + e]))
-                                         : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sum[e] = res[e] + v[e];
-            if (full) {
-              if (p.out_f32p) store4(p.out_f32p + o, sum[0], sum[1], sum[2], sum[3]);
-              if (p.out_model) store4((T*)p.out_model + o, sum[0], sum[1], sum[2], sum[3]);
-              if (p.out_raw) store4(p.out_raw + o, v[0], v[1], v[2], v[3]);
-            } else {
-              for (int e = 0; e < 4 && col + e < p.N; ++e) {
-                if (p.out_f32p) p.out_f32p[o + e] = sum[e];
-                if (p.out_model) ((T*)p.out_model)[o + e] = from_f32<T>(sum[e]);
-                if (p.out_raw) p.out_raw[o + e] = v[e];
-              }
-            }
-          } else {
-            float w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (EPI == EPI_RELU2) {
-                const float rl = fmaxf(v[e], 0.f);
-                w[e] = rl * rl;
-              } else if constexpr (EPI == EPI_XIELU) {
-                w[e] = xielu_f(v[e], p.xa_p, p.xa_n, p.xbeta, p.xeps);
-              } else {  // EPI_MOE_DOWN
-                w[e] = wrow * v[e];
-              }
-            }
-            if (full) {
-              store4((T*)p.out + o, w[0], w[1], w[2], w[3]);
-            } else {
-              for (int e = 0; e < 4 && col + e < p.N; ++e)
-                ((T*)p.out)[o + e] = from_f32<T>(w[e]);
-            }
-          }
+          epi_quad<T, EPI>(p, orow, col, v, wrow);
         }
+    }
+  }
+}
+
+// Tail-split fixup: split tile j is tile F + j of the grid (F = whole
+// tiles); its two K halves are float32 [BM][BN] tiles at split_ws[2j] and
+// split_ws[2j + 1].  Their sum (first half + second half) goes through the
+// same epilogue as a whole tile.
+template <typename T, int EPI, int BM, int BN, int WN>
+__global__ void __launch_bounds__(256) split_fixup_kernel(const GemmParams p) {
+  constexpr bool PAIRED = (EPI == EPI_SWIGLU);
+  const int n_per_tile = PAIRED ? BN / 2 : BN;
+  const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
+  const int num_m = (p.M + BM - 1) / BM;
+  const int j = blockIdx.x;
+  int mt, nt;
+  tile_coords(num_m * num_n - p.split_tiles + j, num_m, num_n, mt, nt);
+  const float* w0 = p.split_ws + (size_t)(2 * j) * BM * BN;
+  const float* w1 = w0 + (size_t)BM * BN;
+  for (int qd = threadIdx.x; qd < BM * BN / 4; qd += 256) {
+    const int r = qd / (BN / 4), c = (qd % (BN / 4)) * 4;
+    const int row = mt * BM + r;
+    if (row >= p.M) continue;
+    const float* a0 = w0 + r * BN + c;
+    const float* a1 = w1 + r * BN + c;
+    if constexpr (PAIRED) {
+      const int cc = c % WN;
+      if (cc >= WN / 2) continue;
+      float g[4], u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g[e] = a0[e] + a1[e];
+        u[e] = a0[WN / 2 + e] + a1[WN / 2 + e];
+      }
+      swiglu_quad<T>(p, (T*)p.out + (int64_t)row * p.ldo, nt * (BN / 2) + (c / WN) * (WN / 2) + cc,
+                     g, u);
+    } else {
+      const int col = nt * BN + c;
+      if (col >= p.N) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = a0[e] + a1[e];
+      epi_quad<T, EPI>(p, (int64_t)row * p.ldo, col, v, 1.0f);
     }
   }
 }
 
 // ------------------------------------------------------------ launchers
 
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      n = v;
+    if (n <= 0) n = 256;
+  }
+  return n;
+}
+
 template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
-static hipError_t launch(const GemmParams& p, int max_rows, hipStream_t s) {
+static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   const int n_per_tile = (EPI == EPI_SWIGLU) ? TL::BN / 2 : TL::BN;
-  const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
+  const int num_n = (p0.N + n_per_tile - 1) / n_per_tile;
   if (GROUPED) {
-    const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p.ngroups;
+    const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p0.ngroups;
     hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(max_tiles * num_n),
-                       dim3(TL::NT), 0, s, p);
-  } else {
-    const int num_m = (p.M + TL::BM - 1) / TL::BM;
-    hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>),
-                       dim3(num_m * num_n), dim3(TL::NT), 0, s, p);
+                       dim3(TL::NT), 0, s, p0);
+    return hipGetLastError();
+  }
+  GemmParams p = p0;
+  p.split_tiles = 0;
+  const int num_m = (p.M + TL::BM - 1) / TL::BM;
+  const int tiles = num_m * num_n;
+  if constexpr (EPI != EPI_QKV) {
+    // tail split: the last wave would leave more than half of the CUs idle.
+    // The partial tiles and the fixup cost a roughly fixed ~30 us, so only
+    // long K (>= 128 stages; measured: 288 stages gain 10%, 40 and 64 lose)
+    const int cus = cu_count();
+    const int rem = tiles % cus;
+    const int nk = (p.K + TL::BK - 1) / TL::BK;
+    if (tiles > cus && rem > 0 && rem <= cus / 2 && nk >= 128 && p.split_ws != nullptr &&
+        (size_t)rem * 2 * TL::BM * TL::BN * sizeof(float) <= p.split_ws_bytes)
+      p.split_tiles = rem;
+  }
+  hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(tiles + p.split_tiles),
+                     dim3(TL::NT), 0, s, p);
+  if constexpr (EPI != EPI_QKV) {
+    if (p.split_tiles > 0)
+      hipLaunchKernelGGL((split_fixup_kernel<T, EPI, TL::BM, TL::BN, TL::WN>),
+                         dim3(p.split_tiles), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -66,6 +66,14 @@ struct GemmParams {
   const void* q_norm_w; const void* k_norm_w;
   const float* rope_cos; const float* rope_sin;   // [S_max, hd/2]
   float eps;
+  // Tail split (chosen by gemm(); the caller only provides the scratch):
+  // when the last wave of tiles would leave more than half of the CUs idle,
+  // its split_tiles tiles are computed as two K halves whose float32
+  // partial tiles go to split_ws; a fixup kernel adds the halves in a fixed
+  // order and applies the epilogue.
+  float* split_ws;
+  size_t split_ws_bytes;
+  int split_tiles;
 };
 
 hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
