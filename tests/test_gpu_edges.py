@@ -221,3 +221,38 @@ def test_split_tail_tiles():
     a_tap = host(d["attention_norm_output"][0])
     att = ob.attention_sublayer(x64[0], a_tap, None, W, cfg, rows)
     assert rel_err(host(d["layer_mid"][0][torch.from_numpy(rows).cuda()]), att["layer_mid"]) <= BF16_BAR
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_trinity_nano_moe_shape(dtype):
+    """The afmoe page's Nano shape: 128 routed experts of width 256, top 8,
+    hidden 1024, one shared expert (narrow experts: a harder grouped GEMM)."""
+    w = afmoe("afmoe_nano", dtype, B=2, S=96, E=128, top_k=8, H=1024, nh=8, nkv=2,
+              hd=128, I_e=256, window=0, head_gate=8)
+    CHECK[dtype](Run(w))
+
+
+def test_stack_of_blocks_on_one_handle():
+    """A stack: the float32 output of block 1 is the input of block 2 (other
+    weights), both on one handle and one workspace, against the oracle
+    applied twice."""
+    w1 = llama("llama_stack", "f32", B=2, S=70, seed=50)
+    w2 = w1.replace(seed=51)
+    r1, r2 = Run(w1), Run(w2)
+    y1 = r1.forward(["layer_output"])
+    x2 = r1.forward(on_device=True)["y_raw"]
+    # block 2 on block 1's handle: same shapes, block 2's weights
+    from transformer_decoder_block_amd import binding as L
+    y = torch.empty_like(x2)
+    io = L.blk_io(x=x2.data_ptr(), attention_mask=None, batch=w1.B, seq=w1.S, y=y.data_ptr())
+    st = L.blk_forward(r1.block.h, io, r2.block.w, None,
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == L.BLK_OK, L.blk_last_error()
+    from tests.blockrun import host
+    cfg = w1.as_dict()
+    for b in range(w1.B):
+        h1 = ob.block_forward(r1.x64()[b], None, r1.W64, cfg)["layer_output"]
+        assert rel_err(y1["layer_output"][b], h1) <= F32_BAR
+        h2 = ob.block_forward(h1, None, r2.W64, cfg)["layer_output"]
+        assert rel_err(host(y[b]), h2) <= F32_BAR

@@ -138,16 +138,21 @@ struct Frags<bf16, AM, AN, KB> {
   static constexpr int STEPS = KB / 64;  // 32-wide k-steps per stage
   typedef f32x4 Blk;
   bf16x8 a[AM], b[AN];
-  // k-step ks: lane quarter q (= lane / 16) reads chunk 4 ks + q of its row
+  // k-step ks: lane quarter q (= lane / 16) reads chunk 4 ks + q of its row.
+  // Read order follows the MFMA order (row block i outer, column block j
+  // inner): b[0], a[0], the other b, then the other a, so the first MFMA
+  // waits for two reads rather than for all of a.
   __device__ __forceinline__ void load(const bf16* As, const bf16* Bs, int arow0,
                                        int brow0, int lane, int ks) {
     const int r = lane & 15, c = 4 * ks + (lane >> 4);
+    b[0] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16, KB>(brow0 + r, c));
+    a[0] = *reinterpret_cast<const bf16x8*>(As + swz<bf16, KB>(arow0 + r, c));
 #pragma unroll
-    for (int i = 0; i < AM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16, KB>(arow0 + i * 16 + r, c));
-#pragma unroll
-    for (int j = 0; j < AN; ++j)
+    for (int j = 1; j < AN; ++j)
       b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz<bf16, KB>(brow0 + j * 16 + r, c));
+#pragma unroll
+    for (int i = 1; i < AM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(As + swz<bf16, KB>(arow0 + i * 16 + r, c));
   }
   __device__ __forceinline__ void mma(f32x4 (&acc)[AM][AN]) const {
 #pragma unroll
