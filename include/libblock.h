@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define BLK_ABI_VERSION 1
+#define BLK_ABI_VERSION 2
 
 typedef enum blk_status {
   BLK_OK = 0,
@@ -158,6 +158,27 @@ typedef struct blk_tap {
  *  expert_indices        [B,S,top_k]    I32, slots in descending biased
  *                                       score, ties to the lower index (MOE)
  *  expert_weights        [B,S,top_k]    F32 (MOE)
+ * Interior values of the attention and the MLP (support() tables, the
+ * attention and mlp rows):
+ *  attention_queries     [B,nh,S,hd]    model dtype: the queries the
+ *                                       attention reads (after q norm and
+ *                                       rotary)
+ *  attention_keys        [B,nkv,S,hd]   model dtype (after k norm, rotary)
+ *  attention_values      [B,nkv,S,hd]   model dtype
+ *  attention_probabilities [B,nh,S,S]   F32, softmax rows, 0 where masked
+ *                                       (a row with no visible key is 0)
+ *  attention_head_outputs [B,S,nh,hd]   model dtype, before the head gate
+ *  attention_premix      [B,S,nh*hd]    model dtype: the o_proj operand
+ *                                       (after the head gate)
+ *  mlp_neurons           [B,S,I]        model dtype: the down projection's
+ *                                       operand (SWIGLU, RELU2, XIELU)
+ *  expert_outputs        [B,S,top_k,H]  model dtype: each slot's expert
+ *                                       output times its weight (MOE)
+ *  routed_output         [B,S,H]        F32: the sum of the slots (MOE)
+ *  shared_expert_output  [B,S,H]        F32 (MOE with a shared expert)
+ * The interior taps are produced by extra copies or kernels on the same
+ * stream (the probabilities and the ungated head outputs recompute the
+ * attention); requesting them slows the call down.
  */
 typedef struct blk_taps {
   blk_tap layer_input;
@@ -171,6 +192,16 @@ typedef struct blk_taps {
   blk_tap router_logits;
   blk_tap expert_indices;
   blk_tap expert_weights;
+  blk_tap attention_queries;
+  blk_tap attention_keys;
+  blk_tap attention_values;
+  blk_tap attention_probabilities;
+  blk_tap attention_head_outputs;
+  blk_tap attention_premix;
+  blk_tap mlp_neurons;
+  blk_tap expert_outputs;
+  blk_tap routed_output;
+  blk_tap shared_expert_output;
 } blk_taps;
 
 /* The residual stream in and out. */

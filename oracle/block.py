@@ -346,8 +346,10 @@ def attention_sublayer(x, a, key_mask, W, cfg, rows=None):
     Only keys at positions <= max(rows) are projected (later keys are
     invisible to every requested row).
 
-    Returns a dict of the [support] values at ``rows``: attention_scores
-    [nh, R, K], attention_probabilities, attention_head_outputs [R, nh, hd],
+    Returns a dict of the [support] values at ``rows``: attention_queries
+    [nh, R, hd], attention_keys and attention_values [nkv, K, hd] (K = the
+    keys up to max(rows)), attention_scores [nh, R, K],
+    attention_probabilities, attention_head_outputs [R, nh, hd],
     attention_premix, attention_output, layer_mid.
     """
     S = x.shape[0]
@@ -381,6 +383,9 @@ def attention_sublayer(x, a, key_mask, W, cfg, rows=None):
         attn_out = o
     mid = np.asarray(x, F64)[rows] + attn_out
     return {
+        "attention_queries": q,
+        "attention_keys": k,
+        "attention_values": v,
         "attention_scores": scores,
         "attention_probabilities": probs,
         "attention_head_outputs": head_out,

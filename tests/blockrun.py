@@ -73,6 +73,16 @@ class Run:
             "router_logits": ((B, S, w.E), self.tdt, self.mdt),
             "expert_indices": ((B, S, w.top_k), torch.int32, L.BLK_I32),
             "expert_weights": ((B, S, w.top_k), torch.float32, L.BLK_F32),
+            "attention_queries": ((B, w.nh, S, w.hd), self.tdt, self.mdt),
+            "attention_keys": ((B, w.nkv, S, w.hd), self.tdt, self.mdt),
+            "attention_values": ((B, w.nkv, S, w.hd), self.tdt, self.mdt),
+            "attention_probabilities": ((B, w.nh, S, S), torch.float32, L.BLK_F32),
+            "attention_head_outputs": ((B, S, w.nh, w.hd), self.tdt, self.mdt),
+            "attention_premix": ((B, S, w.nh * w.hd), self.tdt, self.mdt),
+            "mlp_neurons": ((B, S, w.I), self.tdt, self.mdt),
+            "expert_outputs": ((B, S, w.top_k, w.H), self.tdt, self.mdt),
+            "routed_output": ((B, S, w.H), torch.float32, L.BLK_F32),
+            "shared_expert_output": ((B, S, w.H), torch.float32, L.BLK_F32),
         }
         tapt = {}
         for n in taps:

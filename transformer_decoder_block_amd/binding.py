@@ -64,7 +64,12 @@ class blk_tap(C.Structure):
 
 TAP_NAMES = ["layer_input", "attention_norm_output", "attention_scores",
              "layer_mid", "mlp_input", "layer_output", "attention_output",
-             "mlp_output", "router_logits", "expert_indices", "expert_weights"]
+             "mlp_output", "router_logits", "expert_indices", "expert_weights",
+             "attention_queries", "attention_keys", "attention_values",
+             "attention_probabilities", "attention_head_outputs", "attention_premix",
+             "mlp_neurons", "expert_outputs", "routed_output", "shared_expert_output"]
+
+ABI_VERSION = 2  # the BLK_ABI_VERSION these structs mirror
 
 
 class blk_taps(C.Structure):
@@ -93,6 +98,10 @@ def load():
             f"{LIB_PATH} is missing: build it with "
             "`python -m transformer_decoder_block_amd.build`")
     lib = C.CDLL(LIB_PATH, mode=os.RTLD_NOW)  # unresolved symbols fail here
+    lib.blk_abi_version.restype = C.c_int32
+    if lib.blk_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI {lib.blk_abi_version()}, the binding "
+                           f"mirrors {ABI_VERSION}: rebuild it")
     H = C.POINTER(blk_handle)
     lib.blk_create.argtypes = [C.POINTER(blk_config), C.POINTER(H)]
     lib.blk_create.restype = C.c_int

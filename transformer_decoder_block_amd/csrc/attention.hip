@@ -25,6 +25,7 @@
 // Workgroups are numbered so that the query heads sharing one KV head and
 // one query block are consecutive and land on the same XCD (shared K/V in
 // its L2), and the heaviest (latest) query blocks start first.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -647,6 +648,71 @@ __global__ void __launch_bounds__(256) scores_kernel(const AttnParams p, float* 
   scores[(((int64_t)b * p.nh + h) * p.S + i) * p.S + j] = vis ? acc * p.scale : -INFINITY;
 }
 
+// The attention_probabilities tap: softmax over each query row of the
+// visible keys' scores (q.k / sqrt(hd)), 0 at masked keys and on rows with
+// no visible key.  One workgroup per row; the output row holds the scores,
+// then their exponentials, then the probabilities.
+template <typename T, int HD>
+__global__ void __launch_bounds__(256) probs_kernel(const AttnParams p, float* probs) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / p.nh, h = bh % p.nh;
+  const int kvh = h / (p.nh / p.nkv);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const T* qr = (const T*)p.q + (((int64_t)b * p.nh + h) * p.S + i) * HD;
+  float* row = probs + (((int64_t)b * p.nh + h) * p.S + i) * p.S;
+  float mx = -INFINITY;
+  for (int j = tid; j < p.S; j += 256) {
+    const T* kr = (const T*)p.k + (((int64_t)b * p.nkv + kvh) * p.S + j) * HD;
+    bool vis = j <= i;
+    if (p.mask && p.mask[(int64_t)b * p.S + j] == 0) vis = false;
+    if (p.window > 0 && i - j >= p.window) vis = false;
+    float acc = -INFINITY;
+    if (vis) {
+      acc = 0.f;
+      for (int d = 0; d < HD; ++d) acc += to_f32(qr[d]) * to_f32(kr[d]);
+      acc *= p.scale;
+    }
+    row[j] = acc;
+    mx = fmaxf(mx, acc);
+  }
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = tid; j < p.S; j += 256) {
+    const float e = (mx == -INFINITY) ? 0.f : expf(row[j] - mx);
+    row[j] = e;
+    sum += e;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red[wv] = sum;
+  __syncthreads();
+  sum = red[0] + red[1] + red[2] + red[3];
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  for (int j = tid; j < p.S; j += 256) row[j] *= inv;
+}
+
+// The attention_values tap: [B, nkv, S, hd] from the transposed V^T rows
+// (bf16 rows hold each aligned group of 16 keys in the order 0-3, 8-11,
+// 4-7, 12-15).
+template <typename T, int HD>
+__global__ void __launch_bounds__(256) values_kernel(const AttnParams p, T* v) {
+  const int64_t n = (int64_t)p.B * p.nkv * p.S * HD;
+  const int Sp = (p.S + 63) & ~63;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int d = (int)(e % HD);
+    const int64_t r = e / HD;
+    const int sk = (int)(r % p.S);
+    const int64_t bk = r / p.S;  // b * nkv + kv head
+    const int pos = (sizeof(T) == 2) ? ((sk & ~12) | ((sk & 4) << 1) | ((sk & 8) >> 1)) : sk;
+    v[e] = ((const T*)p.vt)[(bk * HD + d) * Sp + pos];
+  }
+}
+
 template <typename T, int HD>
 static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   const int nqb = (p.S + QB - 1) / QB;
@@ -677,6 +743,35 @@ hipError_t attention_scores(DType dt, const AttnParams& p, float* scores, hipStr
   } else {
     if (p.hd == 64) hipLaunchKernelGGL((scores_kernel<float, 64>), grid, dim3(256), 0, s, p, scores);
     else hipLaunchKernelGGL((scores_kernel<float, 128>), grid, dim3(256), 0, s, p, scores);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace blk
+
+namespace blk {
+
+hipError_t attention_probs(DType dt, const AttnParams& p, float* probs, hipStream_t s) {
+  dim3 grid(p.S, p.B * p.nh);
+  if (dt == DType::BF16) {
+    if (p.hd == 64) hipLaunchKernelGGL((probs_kernel<bf16, 64>), grid, dim3(256), 0, s, p, probs);
+    else hipLaunchKernelGGL((probs_kernel<bf16, 128>), grid, dim3(256), 0, s, p, probs);
+  } else {
+    if (p.hd == 64) hipLaunchKernelGGL((probs_kernel<float, 64>), grid, dim3(256), 0, s, p, probs);
+    else hipLaunchKernelGGL((probs_kernel<float, 128>), grid, dim3(256), 0, s, p, probs);
+  }
+  return hipGetLastError();
+}
+
+hipError_t attention_values(DType dt, const AttnParams& p, void* v, hipStream_t s) {
+  const int64_t n = (int64_t)p.B * p.nkv * p.S * p.hd;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  if (dt == DType::BF16) {
+    if (p.hd == 64) hipLaunchKernelGGL((values_kernel<bf16, 64>), dim3(blocks), dim3(256), 0, s, p, (bf16*)v);
+    else hipLaunchKernelGGL((values_kernel<bf16, 128>), dim3(blocks), dim3(256), 0, s, p, (bf16*)v);
+  } else {
+    if (p.hd == 64) hipLaunchKernelGGL((values_kernel<float, 64>), dim3(blocks), dim3(256), 0, s, p, (float*)v);
+    else hipLaunchKernelGGL((values_kernel<float, 128>), dim3(blocks), dim3(256), 0, s, p, (float*)v);
   }
   return hipGetLastError();
 }

@@ -320,11 +320,23 @@ blk_status check_taps(const blk_handle* h, const blk_taps* t) {
       {"router_logits", &t->router_logits, md, moe},
       {"expert_indices", &t->expert_indices, BLK_I32, moe},
       {"expert_weights", &t->expert_weights, BLK_F32, moe},
+      {"attention_queries", &t->attention_queries, md, true},
+      {"attention_keys", &t->attention_keys, md, true},
+      {"attention_values", &t->attention_values, md, true},
+      {"attention_probabilities", &t->attention_probabilities, BLK_F32, true},
+      {"attention_head_outputs", &t->attention_head_outputs, md, true},
+      {"attention_premix", &t->attention_premix, md, true},
+      {"mlp_neurons", &t->mlp_neurons, md, !moe},
+      {"expert_outputs", &t->expert_outputs, md, moe},
+      {"routed_output", &t->routed_output, BLK_F32, moe},
+      {"shared_expert_output", &t->shared_expert_output, BLK_F32,
+       moe && h->cfg.num_shared_experts > 0},
   };
   for (const auto& c : list) {
     if (!c.tap->ptr) continue;
     if (!c.allowed)
-      return fail(BLK_E_CONFIG, std::string("tap ") + c.name + " needs mlp_kind MOE");
+      return fail(BLK_E_CONFIG, std::string("tap ") + c.name +
+                                    " does not exist for this block's mlp_kind");
     if (c.tap->dtype != c.want)
       return fail(BLK_E_DTYPE, std::string("tap ") + c.name + " must be requested as dtype " +
                                    std::to_string(c.want));
@@ -502,6 +514,32 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
   HIP_TRY(attention(dt, ap, s), "attention");
   if (tp.attention_scores.ptr)
     HIP_TRY(attention_scores(dt, ap, (float*)tp.attention_scores.ptr, s), "scores tap");
+  if (tp.attention_probabilities.ptr)
+    HIP_TRY(attention_probs(dt, ap, (float*)tp.attention_probabilities.ptr, s), "probs tap");
+  if (tp.attention_queries.ptr)
+    HIP_TRY(hipMemcpyAsync(tp.attention_queries.ptr, h->q, (size_t)T * nh * hd * es,
+                           hipMemcpyDeviceToDevice, s), "queries tap");
+  if (tp.attention_keys.ptr)
+    HIP_TRY(hipMemcpyAsync(tp.attention_keys.ptr, h->k, (size_t)T * nkv * hd * es,
+                           hipMemcpyDeviceToDevice, s), "keys tap");
+  if (tp.attention_values.ptr)
+    HIP_TRY(attention_values(dt, ap, tp.attention_values.ptr, s), "values tap");
+  if (tp.attention_premix.ptr)
+    HIP_TRY(hipMemcpyAsync(tp.attention_premix.ptr, h->premix, (size_t)T * nh * hd * es,
+                           hipMemcpyDeviceToDevice, s), "premix tap");
+  if (tp.attention_head_outputs.ptr) {
+    if (G) {  // the same attention without the head gate
+      AttnParams hp = ap;
+      hp.gate = nullptr;
+      hp.G = 0;
+      hp.out = tp.attention_head_outputs.ptr;
+      HIP_TRY(attention(dt, hp, s), "head outputs tap");
+    } else {
+      HIP_TRY(hipMemcpyAsync(tp.attention_head_outputs.ptr, h->premix,
+                             (size_t)T * nh * hd * es, hipMemcpyDeviceToDevice, s),
+              "head outputs tap");
+    }
+  }
 
   // (4) o_proj (+ residual) and the MLP-input norm
   {
@@ -582,6 +620,10 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     }
     prof_mark(h, "gemm_up", s);
     HIP_TRY(gemm(dt, epi, p, T, s), "mlp up gemm");
+    if (tp.mlp_neurons.ptr)
+      HIP_TRY(hipMemcpy2DAsync(tp.mlp_neurons.ptr, (size_t)I * es, h->neur,
+                               neuron_ld(I) * es, (size_t)I * es, T, hipMemcpyDeviceToDevice, s),
+              "neurons tap");
 
     GemmParams d = gp0(h);
     d.M = T;
@@ -742,6 +784,15 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     prof_mark(h, "gemm_shared_down", s);
     HIP_TRY(gemm(dt, EPI_STORE, d, T, s), "shared down gemm");
   }
+  if (tp.expert_outputs.ptr)
+    HIP_TRY(hipMemcpyAsync(tp.expert_outputs.ptr, h->stage, (size_t)T * kk * H * es,
+                           hipMemcpyDeviceToDevice, s), "expert outputs tap");
+  if (tp.routed_output.ptr)
+    HIP_TRY(moe_sum_slots(dt, h->stage, kk, (float*)tp.routed_output.ptr, T, H, s),
+            "routed output tap");
+  if (tp.shared_expert_output.ptr)
+    HIP_TRY(hipMemcpyAsync(tp.shared_expert_output.ptr, h->mlp_raw, (size_t)T * H * 4,
+                           hipMemcpyDeviceToDevice, s), "shared expert output tap");
   prof_mark(h, "combine", s);
   HIP_TRY(moe_combine(dt, h->stage, Ish > 0 ? h->mlp_raw : nullptr, h->mid,
                       w->w_post_mlp_norm, kk, (float*)tp.mlp_output.ptr,

@@ -93,6 +93,11 @@ hipError_t norm_add_norm(DType dt, const float* o, const void* x,
 
 // MoE tail: raw = sum_k stage[t, k] + shared[t]; mo = norm_post(raw);
 // out = mid + mo -> out_f32 (may be null), y (model dtype).
+// routed[t] = sum over slots 0..k-1 (in that order) of stage[t*k + slot]
+// (the routed_output tap)
+hipError_t moe_sum_slots(DType dt, const void* stage, int top_k, float* routed, int rows,
+                         int H, hipStream_t s);
+
 hipError_t moe_combine(DType dt, const void* stage, const float* shared,
                        const float* mid, const void* g_post, int top_k,
                        float* mlp_out, float* out_f32, void* y, int rows,
@@ -108,6 +113,11 @@ struct AttnParams {
   float scale;            // 1/sqrt(hd)
 };
 hipError_t attention(DType dt, const AttnParams& p, hipStream_t s);
+
+// probs[b,h,i,:] = softmax of row i's visible scores, 0 elsewhere (tap only)
+hipError_t attention_probs(DType dt, const AttnParams& p, float* probs, hipStream_t s);
+// v[b,kvh,s,:] from the transposed V^T (tap only)
+hipError_t attention_values(DType dt, const AttnParams& p, void* v, hipStream_t s);
 
 // scores[b,h,i,j] = q.k/sqrt(hd) or -inf (tap only)
 hipError_t attention_scores(DType dt, const AttnParams& p, float* scores,

@@ -242,6 +242,32 @@ static hipError_t comb_dispatch(DType dt, const void* stage, const float* shared
   return hipGetLastError();
 }
 
+template <typename T>
+__global__ void __launch_bounds__(256) sum_slots_kernel(const T* __restrict__ stage, int top_k,
+                                                        float* __restrict__ routed, int rows,
+                                                        int H) {
+  const int64_t n = (int64_t)rows * H;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / H, c = e % H;
+    float acc = 0.f;
+    for (int s = 0; s < top_k; ++s) acc += to_f32(stage[(r * top_k + s) * H + c]);
+    routed[e] = acc;
+  }
+}
+
+hipError_t moe_sum_slots(DType dt, const void* stage, int top_k, float* routed, int rows,
+                         int H, hipStream_t s) {
+  const int64_t n = (int64_t)rows * H;
+  const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+  if (dt == DType::BF16)
+    hipLaunchKernelGGL((sum_slots_kernel<bf16>), dim3(blocks), dim3(256), 0, s,
+                       (const bf16*)stage, top_k, routed, rows, H);
+  else
+    hipLaunchKernelGGL((sum_slots_kernel<float>), dim3(blocks), dim3(256), 0, s,
+                       (const float*)stage, top_k, routed, rows, H);
+  return hipGetLastError();
+}
+
 hipError_t moe_combine(DType dt, const void* stage, const float* shared, const float* mid,
                        const void* g_post, int top_k, float* mlp_out, float* out_f32,
                        void* y, int rows, int H, float eps, int sandwich, hipStream_t s) {
