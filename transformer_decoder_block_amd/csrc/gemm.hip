@@ -346,6 +346,48 @@ __device__ __forceinline__ void epi_quad(const GemmParams& p, int64_t orow, int 
   }
 }
 
+// Residual epilogue of a wave sub-tile whose columns all exist: the
+// residual quads of row block i + 1 are loaded before the sums of block i
+// are stored, so the loads of a block overlap the stores of the one before
+// (every residual element is loaded before the same element is stored,
+// which also holds when the output is the residual buffer).
+template <typename T, typename R, class L, class ACC>
+__device__ __forceinline__ void resid_tile(const GemmParams& p, const ACC& acc,
+                                           const int64_t (&orow)[L::AM],
+                                           const bool (&rok)[L::AM], int col0, int lane) {
+  constexpr int AM = L::AM, NQ = L::AN * L::QPB;
+  float res[2][NQ][4];
+  auto load_blk = [&](int i, float (&r)[NQ][4]) {
+#pragma unroll
+    for (int j = 0; j < L::AN; ++j)
+#pragma unroll
+      for (int q = 0; q < L::QPB; ++q)
+        load4((const R*)p.resid + orow[i] + col0 + L::col(lane, j, q), r[j * L::QPB + q]);
+  };
+  load_blk(0, res[0]);
+#pragma unroll
+  for (int i = 0; i < AM; ++i) {
+    if (i + 1 < AM) load_blk(i + 1, res[(i + 1) & 1]);
+    if (!rok[i]) continue;
+#pragma unroll
+    for (int j = 0; j < L::AN; ++j)
+#pragma unroll
+      for (int q = 0; q < L::QPB; ++q) {
+        const int64_t o = orow[i] + col0 + L::col(lane, j, q);
+        const float* r = res[i & 1][j * L::QPB + q];
+        float sum[4], v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * q + e];
+          sum[e] = r[e] + v[e];
+        }
+        if (p.out_f32p) store4(p.out_f32p + o, sum[0], sum[1], sum[2], sum[3]);
+        if (p.out_model) store4((T*)p.out_model + o, sum[0], sum[1], sum[2], sum[3]);
+        if (p.out_raw) store4(p.out_raw + o, v[0], v[1], v[2], v[3]);
+      }
+  }
+}
+
 // SwiGLU quad: neurons col..col+3 of one row from their gate and up values.
 template <typename T>
 __device__ __forceinline__ void swiglu_quad(const GemmParams& p, T* orow, int col,
@@ -790,28 +832,67 @@ gemm_kernel(const GemmParams p) {
     }
     return;
   } else {
+    // The lane's rows: output offsets (and for the MoE down projection the
+    // slot's row and weight) are all loaded before the first store, so
+    // their latency is paid once.  Rows past the tile's end are clamped to
+    // a valid row for the loads and never stored.
+    int64_t orow[AM];
+    float wrow[AM];
+    bool rok[AM];
 #pragma unroll
     for (int i = 0; i < AM; ++i) {
       const int lr = lrow0 + L::row(lane, i);
-      if (lr >= row_count) continue;
-      const int64_t row = row_begin + lr;
-      int64_t orow = row * p.ldo;
-      float wrow = 1.0f;
-      if constexpr (EPI == EPI_MOE_DOWN) {
-        const int pair = p.row_pair[row];
-        orow = (int64_t)pair * p.ldo;
-        wrow = p.pair_weight[pair];
+      rok[i] = lr < row_count;
+      const int64_t row = row_begin + (rok[i] ? lr : 0);
+      orow[i] = row * p.ldo;
+      wrow[i] = 1.0f;
+      if constexpr (EPI == EPI_MOE_DOWN) orow[i] = p.row_pair[row];
+    }
+    if constexpr (EPI == EPI_MOE_DOWN) {
+#pragma unroll
+      for (int i = 0; i < AM; ++i) {
+        wrow[i] = p.pair_weight[orow[i]];
+        orow[i] *= p.ldo;
       }
+    }
+    const int col0 = nt * BN + wn * WN;
+    if (col0 + WN <= p.N) {
+      // every column of the wave's sub-tile exists: no per-quad tests
+      if constexpr (EPI == EPI_RESID) {
+        if (p.resid_f32)
+          resid_tile<T, float, L>(p, acc, orow, rok, col0, lane);
+        else
+          resid_tile<T, T, L>(p, acc, orow, rok, col0, lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < AM; ++i) {
+          if (!rok[i]) continue;
+#pragma unroll
+          for (int j = 0; j < AN; ++j)
+#pragma unroll
+            for (int q = 0; q < QPB; ++q) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+              epi_quad<T, EPI>(p, orow[i], col0 + L::col(lane, j, q), v, wrow[i]);
+            }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < AM; ++i) {
+      if (!rok[i]) continue;
 #pragma unroll
       for (int j = 0; j < AN; ++j)
 #pragma unroll
         for (int q = 0; q < QPB; ++q) {
-          const int col = nt * BN + wn * WN + L::col(lane, j, q);
+          const int col = col0 + L::col(lane, j, q);
           if (col >= p.N) continue;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          epi_quad<T, EPI>(p, orow, col, v, wrow);
+          epi_quad<T, EPI>(p, orow[i], col, v, wrow[i]);
         }
     }
   }
