@@ -134,8 +134,9 @@ hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T,
 hipError_t moe_dispatch(const int* idx, int T, int k, int E, int* gcnt,
                         int* goff, int* row_token, int* row_pair, int* hist,
                         hipStream_t s);
+constexpr int DISPATCH_CHUNK = 256;  // (token, slot) pairs per dispatch chunk
 inline int64_t dispatch_hist_ints(int64_t npairs, int E) {
-  return ((npairs + 1023) / 1024) * E;
+  return ((npairs + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK) * E;
 }
 
 }  // namespace blk

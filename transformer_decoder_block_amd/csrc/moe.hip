@@ -93,7 +93,7 @@ hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T, int 
   return hipGetLastError();
 }
 
-constexpr int DCHUNK = 1024;  // pairs per dispatch chunk
+constexpr int DCHUNK = DISPATCH_CHUNK;  // pairs per dispatch chunk
 
 // hist[e * nchunks + c] = number of pairs of chunk c routed to expert e
 // (integer LDS atomics: the count does not depend on their order).
@@ -153,18 +153,32 @@ __global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx
   const int c = blockIdx.x, l = threadIdx.x;
   const int p0 = c * DCHUNK;
   const int n = min(DCHUNK, npairs - p0);
-  // first row of each expert's group: exclusive scan of the totals
-  if (l == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = acc;
-      acc += gcnt[e];
+  // first row of each expert's group: exclusive scan of the totals (lane l
+  // owns experts 4l .. 4l+3), plus this chunk's offset inside the group
+  {
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * l + q;
+      cnt[q] = e < E ? gcnt[e] : 0;
+      sum += cnt[q];
     }
-  }
-  __syncthreads();
-  for (int e = l; e < E; e += 64) {
-    if (c == 0) goff[e] = base[e];
-    base[e] += hist[e * nchunks + c];
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (l >= o) inc += v;
+    }
+    int ex = inc - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * l + q;
+      if (e < E) {
+        if (c == 0) goff[e] = ex;
+        base[e] = ex + hist[e * nchunks + c];
+      }
+      ex += cnt[q];
+    }
   }
   __syncthreads();
   for (int r0 = 0; r0 < n; r0 += 64) {

@@ -109,35 +109,88 @@ __global__ void __launch_bounds__(256) norm_add_norm_kernel(
   }
 }
 
-// raw = sum over slots 0..k-1 (in that order) of stage[t*k + slot] + shared[t]
+// Eight consecutive elements kept as loaded (bf16: 16 bytes) until added.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  uint4 r;
+  __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void add_to(float* f) const {
+    float t[8];
+    unpack8(r, t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] += t[i];
+  }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void add_to(float* f) const {
+    f[0] += a.x; f[1] += a.y; f[2] += a.z; f[3] += a.w;
+    f[4] += b.x; f[5] += b.y; f[6] += b.z; f[7] += b.w;
+  }
+};
+
+// raw = shared[t] + the slots 0..k-1 in that order (stage[t*k + slot]).
+// The slot loads of a row go out several slots at a time for all of the
+// lane's chunks before any is added, so a wave keeps many loads in flight;
+// the sum order is fixed.
 template <typename T, int MAXCH>
 __global__ void __launch_bounds__(256) moe_combine_kernel(
     const T* __restrict__ stage, const float* __restrict__ shared,
     const float* __restrict__ mid, const T* __restrict__ g_post, int top_k,
     float* __restrict__ mlp_out, float* __restrict__ out_f32, T* __restrict__ y,
     int rows, int H, float eps, int sandwich) {
+  // slots per batch of loads; the residual row is loaded up front when
+  // the registers allow
+  constexpr int SU = MAXCH >= 16 ? 1 : (MAXCH >= 8 ? 2 : 4);
+  constexpr bool PRE_MID = MAXCH <= 4;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t base = (int64_t)row * H;
-  float v[MAXCH][8];
-  float ss = 0.f;
+  float v[MAXCH][8], mv[PRE_MID ? MAXCH : 1][8];
 #pragma unroll
   for (int j = 0; j < MAXCH; ++j) {
     const int c = (lane + 64 * j) * 8;
     if (c < H) {
-      float t[8];
+      if constexpr (PRE_MID) load8(mid + base + c, mv[j]);
       if (shared) {
         load8(shared + base + c, v[j]);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
       }
-      for (int s = 0; s < top_k; ++s) {
-        load8(stage + ((int64_t)row * top_k + s) * H + c, t);
+    }
+  }
+  for (int s0 = 0; s0 < top_k; s0 += SU) {
+    Raw8<T> t[MAXCH][SU];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[j][i] += t[i];
-      }
+    for (int j = 0; j < MAXCH; ++j) {
+      const int c = (lane + 64 * j) * 8;
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if (c < H && s0 + u < top_k)
+          t[j][u].load(stage + ((int64_t)row * top_k + s0 + u) * H + c);
+    }
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+      const int c = (lane + 64 * j) * 8;
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if (c < H && s0 + u < top_k) t[j][u].add_to(v[j]);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXCH; ++j) {
+    const int c = (lane + 64 * j) * 8;
+    if (c < H) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss += v[j][i] * v[j][i];
     }
@@ -151,16 +204,22 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(
   for (int j = 0; j < MAXCH; ++j) {
     const int c = (lane + 64 * j) * 8;
     if (c < H) {
-      float gv[8], mv[8];
       if (sandwich) {
+        float gv[8];
         load8(g_post + c, gv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[j][i] = gv[i] * (v[j][i] * inv);
       }
       if (mlp_out) store8(mlp_out + base + c, v[j]);
-      load8(mid + base + c, mv);
+      float m8[8];
+      if constexpr (PRE_MID) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = mv[i] + v[j][i];
+        for (int i = 0; i < 8; ++i) m8[i] = mv[j][i];
+      } else {
+        load8(mid + base + c, m8);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = m8[i] + v[j][i];
       if (out_f32) store8(out_f32 + base + c, v[j]);
       store8(y + base + c, v[j]);
     }
