@@ -617,14 +617,8 @@ gemm_kernel(const GemmParams p) {
   int mt, nt, row_begin = 0, row_count = p.M, group = 0;
   int split_slot = -1;  // >= 0: this block computes K half (split_slot & 1) of a tail tile
   if constexpr (GROUPED) {
-    // one dimension: consecutive ids (which the renumbering keeps on one
-    // XCD) are the N tiles of one M tile, so the gathered A rows are read
-    // once and an expert's weights are shared by its M tiles in that L2
-    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int t = id / num_n;
-    nt = id % num_n;
     // M tiles per group, exclusive prefix sums in LDS (the first wave: lane
-    // j owns groups 4j .. 4j+3, at most 256 groups); the group of tile t is
+    // j owns groups 4j .. 4j+3, at most 256 groups); the group of a tile is
     // then found by a binary search
     int* tpre = reinterpret_cast<int*>(smem + SMEM0);
     if (wave == 0) {
@@ -650,7 +644,16 @@ gemm_kernel(const GemmParams p) {
       if (lane == 63) tpre[256] = inc;
     }
     __syncthreads();
-    if (t >= tpre[256]) return;  // idle tile of the worst-case grid
+    // one dimension over the real tiles (the grid is sized for the worst
+    // case): consecutive ids, which the renumbering keeps on one XCD, are
+    // the N tiles of one M tile, so the gathered A rows are read once and an
+    // expert's weights are shared by its M tiles in that L2.  The surplus
+    // workgroups are the highest block numbers, spread evenly over the XCDs.
+    const int real = tpre[256] * num_n;
+    if ((int)blockIdx.x >= real) return;
+    const int id = xcd_contiguous(blockIdx.x, real);
+    const int t = id / num_n;
+    nt = id % num_n;
     int lo = 0, hi = p.ngroups;  // tpre[lo] <= t < tpre[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
