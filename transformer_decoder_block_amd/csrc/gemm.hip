@@ -33,6 +33,8 @@
 // columns 4*(l/16)..+3; 32x32 blocks: four quads, row l%32, columns
 // 8*q + 4*(l/32)..+3).
 // Fragments of k-step s+1 are read from LDS while the MFMAs of step s run.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -583,6 +585,106 @@ __device__ __forceinline__ void qkv_epilogue(ACC& acc, const GemmParams& p, int 
   }
 }
 
+// Register epilogue of one tile (every EPI but the q/k/v one): each lane
+// stores its quads (four consecutive columns) of the rows it holds.
+template <typename T, class TL, int EPI, class ACC>
+__device__ __forceinline__ void tile_epilogue(const GemmParams& p, ACC& acc, int mt, int nt,
+                                              int row_begin, int row_count, int wm, int wn,
+                                              int lane) {
+  constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
+  constexpr bool PAIRED = (EPI == EPI_SWIGLU);
+  using L = AccL<T, WM, WN>;
+  constexpr int AM = L::AM, AN = L::AN, QPB = L::QPB;
+  const int lrow0 = mt * BM + wm * WM;  // tile-local (group-local) row base
+  if constexpr (PAIRED) {
+    // gate columns are the first half of the wave's columns, up the second
+    const int ncol0 = nt * (BN / 2) + wn * (WN / 2);
+#pragma unroll
+    for (int i = 0; i < AM; ++i) {
+      const int lr = lrow0 + L::row(lane, i);
+      if (lr >= row_count) continue;
+      T* orow = (T*)p.out + (int64_t)(row_begin + lr) * p.ldo;
+#pragma unroll
+      for (int j = 0; j < AN / 2; ++j)
+#pragma unroll
+        for (int q = 0; q < QPB; ++q) {
+          float g[4], u[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g[e] = acc[i][j][4 * q + e];
+            u[e] = acc[i][j + AN / 2][4 * q + e];
+          }
+          swiglu_quad<T>(p, orow, ncol0 + L::col(lane, j, q), g, u);
+        }
+    }
+    return;
+  } else {
+    // The lane's rows: output offsets (and for the MoE down projection the
+    // slot's row and weight) are all loaded before the first store, so
+    // their latency is paid once.  Rows past the tile's end are clamped to
+    // a valid row for the loads and never stored.
+    int64_t orow[AM];
+    float wrow[AM];
+    bool rok[AM];
+#pragma unroll
+    for (int i = 0; i < AM; ++i) {
+      const int lr = lrow0 + L::row(lane, i);
+      rok[i] = lr < row_count;
+      const int64_t row = row_begin + (rok[i] ? lr : 0);
+      orow[i] = row * p.ldo;
+      wrow[i] = 1.0f;
+      if constexpr (EPI == EPI_MOE_DOWN) orow[i] = p.row_pair[row];
+    }
+    if constexpr (EPI == EPI_MOE_DOWN) {
+#pragma unroll
+      for (int i = 0; i < AM; ++i) {
+        wrow[i] = p.pair_weight[orow[i]];
+        orow[i] *= p.ldo;
+      }
+    }
+    const int col0 = nt * BN + wn * WN;
+    if (col0 + WN <= p.N) {
+      // every column of the wave's sub-tile exists: no per-quad tests
+      if constexpr (EPI == EPI_RESID) {
+        if (p.resid_f32)
+          resid_tile<T, float, L>(p, acc, orow, rok, col0, lane);
+        else
+          resid_tile<T, T, L>(p, acc, orow, rok, col0, lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < AM; ++i) {
+          if (!rok[i]) continue;
+#pragma unroll
+          for (int j = 0; j < AN; ++j)
+#pragma unroll
+            for (int q = 0; q < QPB; ++q) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+              epi_quad<T, EPI>(p, orow[i], col0 + L::col(lane, j, q), v, wrow[i]);
+            }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < AM; ++i) {
+      if (!rok[i]) continue;
+#pragma unroll
+      for (int j = 0; j < AN; ++j)
+#pragma unroll
+        for (int q = 0; q < QPB; ++q) {
+          const int col = col0 + L::col(lane, j, q);
+          if (col >= p.N) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          epi_quad<T, EPI>(p, orow[i], col, v, wrow[i]);
+        }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- kernel
 
 template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
@@ -806,97 +908,218 @@ gemm_kernel(const GemmParams p) {
   }
 
   // ---- epilogue: each lane stores its quads (four consecutive columns)
-  const int lrow0 = mt * BM + wm * WM;  // tile-local (group-local) row base
   if constexpr (EPI == EPI_QKV) {
     // each wave stages its heads in its own slice of the (now idle) LDS
+    const int lrow0 = mt * BM + wm * WM;
     T* slice = smem + wave * SLICE;
     qkv_epilogue<T, HDQ, WM, WN>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
     return;
-  } else if constexpr (PAIRED) {
-    // gate columns are the first half of the wave's columns, up the second
-    const int ncol0 = nt * (BN / 2) + wn * (WN / 2);
-#pragma unroll
-    for (int i = 0; i < AM; ++i) {
-      const int lr = lrow0 + L::row(lane, i);
-      if (lr >= row_count) continue;
-      T* orow = (T*)p.out + (int64_t)(row_begin + lr) * p.ldo;
-#pragma unroll
-      for (int j = 0; j < AN / 2; ++j)
-#pragma unroll
-        for (int q = 0; q < QPB; ++q) {
-          float g[4], u[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            g[e] = acc[i][j][4 * q + e];
-            u[e] = acc[i][j + AN / 2][4 * q + e];
-          }
-          swiglu_quad<T>(p, orow, ncol0 + L::col(lane, j, q), g, u);
-        }
-    }
-    return;
   } else {
-    // The lane's rows: output offsets (and for the MoE down projection the
-    // slot's row and weight) are all loaded before the first store, so
-    // their latency is paid once.  Rows past the tile's end are clamped to
-    // a valid row for the loads and never stored.
-    int64_t orow[AM];
-    float wrow[AM];
-    bool rok[AM];
+    tile_epilogue<T, TL, EPI>(p, acc, mt, nt, row_begin, row_count, wm, wn, lane);
+  }
+}
+
+// Persistent form for the register epilogues (every EPI but q/k/v) of the
+// 256x256 tile without a K split.  One workgroup per CU walks the tile ids
+// b, b + G, b + 2G, ... (G = the grid); ids stay on the XCD the block runs
+// on, as in the one-tile-per-block launch.  The first stage of the next
+// tile is issued while the last stage of the current one computes, and its
+// epilogue stores run while that load lands, so a tile boundary does not
+// drain the load pipeline.
+template <typename T, class TL, int EPI, bool GROUPED>
+__global__ void __attribute__((amdgpu_flat_work_group_size(TL::NT, TL::NT),
+                               amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
+gemm_persistent_kernel(const GemmParams p) {
+  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, CH = TL::CH,
+                CPR = TL::CPR, LD = TL::LD, WM = TL::WM, WN = TL::WN,
+                AL = TL::AL, BL = TL::BL, NS = TL::NS, RPI = TL::RPI, KB = TL::KB;
+  static_assert(NS == 2 && EPI != EPI_QKV, "two stages, register epilogue");
+  constexpr int RPB = 256 / KB;
+  constexpr bool PAIRED = (EPI == EPI_SWIGLU);
+  constexpr int MAIN = NS * (BM + BN) * LD;
+  constexpr int SMEM = GROUPED ? MAIN + 257 * 4 / (int)sizeof(T) + 4 : MAIN;
+  __shared__ __attribute__((aligned(1024))) T smem[SMEM];
+  auto As = [&](int b) { return smem + b * (BM * LD); };
+  auto Bs = [&](int b) { return smem + NS * BM * LD + b * (BN * LD); };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  const int n_per_tile = PAIRED ? BN / 2 : BN;
+  const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
+  const int num_m = (p.M + BM - 1) / BM;
+
+  // ---- the tiles: grouped M tiles per expert as in gemm_kernel
+  int* tpre = reinterpret_cast<int*>(smem + MAIN);
+  int total;
+  if constexpr (GROUPED) {
+    if (wave == 0) {
+      int c[4], sum = 0;
 #pragma unroll
-    for (int i = 0; i < AM; ++i) {
-      const int lr = lrow0 + L::row(lane, i);
-      rok[i] = lr < row_count;
-      const int64_t row = row_begin + (rok[i] ? lr : 0);
-      orow[i] = row * p.ldo;
-      wrow[i] = 1.0f;
-      if constexpr (EPI == EPI_MOE_DOWN) orow[i] = p.row_pair[row];
-    }
-    if constexpr (EPI == EPI_MOE_DOWN) {
-#pragma unroll
-      for (int i = 0; i < AM; ++i) {
-        wrow[i] = p.pair_weight[orow[i]];
-        orow[i] *= p.ldo;
+      for (int q = 0; q < 4; ++q) {
+        const int g = 4 * lane + q;
+        c[q] = g < p.ngroups ? (p.gcnt[g] + BM - 1) / BM : 0;
+        sum += c[q];
       }
+      int inc = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+      }
+      int ex = inc - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        tpre[4 * lane + q] = ex;
+        ex += c[q];
+      }
+      if (lane == 63) tpre[256] = inc;
     }
-    const int col0 = nt * BN + wn * WN;
-    if (col0 + WN <= p.N) {
-      // every column of the wave's sub-tile exists: no per-quad tests
-      if constexpr (EPI == EPI_RESID) {
-        if (p.resid_f32)
-          resid_tile<T, float, L>(p, acc, orow, rok, col0, lane);
-        else
-          resid_tile<T, T, L>(p, acc, orow, rok, col0, lane);
+    __syncthreads();
+    total = tpre[256] * num_n;
+  } else {
+    total = num_m * num_n;
+  }
+  auto select = [&](int item, int& mt, int& nt, int& rb, int& rc, int& grp) {
+    const int id = xcd_contiguous(item, total);
+    if constexpr (GROUPED) {
+      const int t = id / num_n;
+      nt = id % num_n;
+      int lo = 0, hi = p.ngroups;  // tpre[lo] <= t < tpre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tpre[mid] <= t) lo = mid;
+        else hi = mid;
+      }
+      grp = lo;
+      mt = t - tpre[lo];
+      rb = p.goff[lo];
+      rc = p.gcnt[lo];
+    } else {
+      tile_coords(id, num_m, num_n, mt, nt);
+      rb = 0;
+      rc = p.M;
+      grp = 0;
+    }
+  };
+
+  // ---- direct-to-LDS load offsets of a tile (as in gemm_kernel)
+  const int lrowi = lane / CPR;
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, p.a_bytes, 0x00020000);
+  static_assert((TL::NW * RPI / RPB) % CPR == 0, "swizzle period divides the load stride");
+  const int k_lane = ((lane % CPR) ^ (((wave * RPI + lrowi) / RPB) & (CPR - 1))) * CH;
+  const bool a_dense = !GROUPED && p.a_gather == nullptr;
+  const uint32_t a_stride = (uint32_t)((int64_t)TL::NW * RPI * p.lda * sizeof(T));
+  auto setup = [&](int mt, int nt, int rb, int rc, int grp, uint32_t (&a_off)[AL],
+                   uint32_t (&b_off)[BL], __amdgpu_buffer_rsrc_t (&rB)[BL]) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int lrow = (TL::NW * i + wave) * RPI + lrowi;
+      const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
+      const int r = mt * BM + lrow;
+      int src = rb + (r < rc ? r : 0);
+      if (p.a_gather) src = p.a_gather[src];
+      a_off[i] = (r < rc) ? (uint32_t)(((int64_t)src * p.lda + kch * CH) * sizeof(T))
+                          : p.a_bytes;
+    }
+    const int64_t gofs = GROUPED ? (int64_t)grp * p.b_group_stride : 0;
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int lbase = (TL::NW * i + wave) * RPI;
+      const int lrow = lbase + lrowi;
+      const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
+      int seg, n;
+      bool ok;
+      if constexpr (PAIRED) {
+        constexpr int half = WN / 2;
+        seg = (lbase % WN) / half;
+        n = nt * (BN / 2) + (lbase / WN) * half + (lrow % WN) % half;
+        ok = n < p.N;
       } else {
-#pragma unroll
-        for (int i = 0; i < AM; ++i) {
-          if (!rok[i]) continue;
-#pragma unroll
-          for (int j = 0; j < AN; ++j)
-#pragma unroll
-            for (int q = 0; q < QPB; ++q) {
-              float v[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-              epi_quad<T, EPI>(p, orow[i], col0 + L::col(lane, j, q), v, wrow[i]);
-            }
-        }
+        const int nb = nt * BN + lbase;
+        seg = 0;
+        while (seg < p.nseg - 1 && nb >= p.seg_end[seg]) ++seg;
+        n = nt * BN + lrow;
+        ok = n < p.N;
+        n -= seg ? p.seg_end[seg - 1] : 0;
       }
-      return;
+      seg = __builtin_amdgcn_readfirstlane(seg);
+      rB[i] = __builtin_amdgcn_make_buffer_rsrc((void*)((const T*)p.B[seg] + gofs), (short)0,
+                                                p.b_bytes[seg], 0x00020000);
+      b_off[i] = ok ? (uint32_t)(((int64_t)n * p.ldb + kch * CH) * sizeof(T)) : p.b_bytes[seg];
     }
+  };
+  auto issue = [&](int kt, int buf, const uint32_t (&a_off)[AL], const uint32_t (&b_off)[BL],
+                   const __amdgpu_buffer_rsrc_t (&rB)[BL]) {
+    const uint32_t ko = kt * BK * sizeof(T);
+    const bool kin = kt * BK + k_lane < p.K;
 #pragma unroll
-    for (int i = 0; i < AM; ++i) {
-      if (!rok[i]) continue;
+    for (int i = 0; i < AL; ++i)
+      load16_to_lds(rA, As(buf) + (TL::NW * i + wave) * RPI * LD,
+                    !kin ? p.a_bytes : (a_dense ? a_off[0] + i * a_stride : a_off[i]) + ko);
+#pragma unroll
+    for (int i = 0; i < BL; ++i)
+      load16_to_lds(rB[i], Bs(buf) + (TL::NW * i + wave) * RPI * LD,
+                    kin ? b_off[i] + ko : 0xffffffffu);
+  };
+
+  using L = AccL<T, WM, WN>;
+  constexpr int AM = L::AM, AN = L::AN, QPB = L::QPB;
+  typename L::Blk acc[AM][AN];
+  const int nk = (p.K + BK - 1) / BK;
+
+  int item = blockIdx.x;
+  if (item >= total) return;
+  int mt, nt, rb, rc, grp;
+  select(item, mt, nt, rb, rc, grp);
+  uint32_t a_off[AL], b_off[BL];
+  __amdgpu_buffer_rsrc_t rB[BL];
+  setup(mt, nt, rb, rc, grp, a_off, b_off, rB);
+  int buf = 0;
+  issue(0, 0, a_off, b_off, rB);
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < AM; ++i)
 #pragma unroll
       for (int j = 0; j < AN; ++j)
 #pragma unroll
-        for (int q = 0; q < QPB; ++q) {
-          const int col = col0 + L::col(lane, j, q);
-          if (col >= p.N) continue;
-          float v[4];
+        for (int r = 0; r < 4 * QPB; ++r) acc[i][j][r] = 0.f;
+    // the next tile, looked up while this one computes
+    const int nitem = item + (int)gridDim.x;
+    const bool more = nitem < total;
+    int mt2 = 0, nt2 = 0, rb2 = 0, rc2 = 0, grp2 = 0;
+    uint32_t a2[AL], b2[BL];
+    __amdgpu_buffer_rsrc_t rB2[BL];
+    if (more) {
+      select(nitem, mt2, nt2, rb2, rc2, grp2);
+      setup(mt2, nt2, rb2, rc2, grp2, a2, b2, rB2);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      // this thread's loads of stage kt (and the stores of the previous
+      // tile's epilogue) are done; after the barrier all threads' are, and
+      // every wave is done with the buffer the next stage refills
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 1 < nk) issue(kt + 1, buf ^ 1, a_off, b_off, rB);
+      else if (more) issue(0, buf ^ 1, a2, b2, rB2);
+      compute_tile<T, AM, AN, KB>(acc, As(buf), Bs(buf), wm * WM, wn * WN, lane);
+      buf ^= 1;
+    }
+    tile_epilogue<T, TL, EPI>(p, acc, mt, nt, rb, rc, wm, wn, lane);
+    if (!more) break;
+    item = nitem;
+    mt = mt2;
+    nt = nt2;
+    rb = rb2;
+    rc = rc2;
+    grp = grp2;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          epi_quad<T, EPI>(p, orow[i], col, v, wrow[i]);
-        }
+    for (int i = 0; i < AL; ++i) a_off[i] = a2[i];
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      b_off[i] = b2[i];
+      rB[i] = rB2[i];
     }
   }
 }
@@ -968,6 +1191,15 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
                        dim3(TL::NT), 0, s, p0);
     return hipGetLastError();
   }
+  constexpr bool PERSIST = TL::BM == 256 && TL::BN == 256 && TL::NS == 2 && TL::WGM == 2 &&
+                           sizeof(T) == 2 && EPI != EPI_QKV;
+  if constexpr (PERSIST && GROUPED) {
+    const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p0.ngroups;
+    const int grid = std::min(max_tiles * num_n, cu_count());
+    hipLaunchKernelGGL((gemm_persistent_kernel<T, TL, EPI, GROUPED>), dim3(grid),
+                       dim3(TL::NT), 0, s, p0);
+    return hipGetLastError();
+  }
   GemmParams p = p0;
   p.split_tiles = 0;
   const int num_m = (p.M + TL::BM - 1) / TL::BM;
@@ -982,6 +1214,13 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
     if (tiles > cus && rem > 0 && rem <= cus / 2 && nk >= 128 && p.split_ws != nullptr &&
         (size_t)rem * 2 * TL::BM * TL::BN * sizeof(float) <= p.split_ws_bytes)
       p.split_tiles = rem;
+  }
+  if constexpr (PERSIST && !GROUPED) {
+    if (p.split_tiles == 0) {
+      hipLaunchKernelGGL((gemm_persistent_kernel<T, TL, EPI, GROUPED>),
+                         dim3(std::min(tiles, cu_count())), dim3(TL::NT), 0, s, p);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(tiles + p.split_tiles),
                      dim3(TL::NT), 0, s, p);
