@@ -256,3 +256,21 @@ def test_stack_of_blocks_on_one_handle():
         assert rel_err(y1["layer_output"][b], h1) <= F32_BAR
         h2 = ob.block_forward(h1, None, r2.W64, cfg)["layer_output"]
         assert rel_err(host(y[b]), h2) <= F32_BAR
+
+
+def test_persistent_gemm_single_stage_tiles():
+    """The MLP up projection at 4096 tokens and width 2104 is 16 x 17 = 272
+    tiles of 256 x 256 with a single K stage (hidden 64): the persistent
+    launch gives 16 of the 256 workgroups a second tile, whose first (and
+    only) stage is loaded during the first tile's only stage."""
+    w = llama("llama_pers", "bf16", B=1, S=4096, H=64, nh=1, nkv=1, hd=64, I=2104)
+    check_bf16(Run(w))
+
+
+def test_persistent_grouped_gemm():
+    """Expert gate/up at 4096 (token, slot) pairs and expert width 2048 is
+    at least 16 x 16 tiles of 256 x 256: the grouped GEMM runs persistent,
+    its tiles found through the per-expert prefix sums."""
+    w = afmoe("afmoe_pers", "bf16", B=1, S=512, E=8, top_k=8, I_e=2048, window=0,
+              head_gate=0)
+    check_bf16(Run(w))
