@@ -37,6 +37,11 @@ reason in the design notes):
   * the per-head sigmoid gate (G = num_heads columns) scales every channel of
     its head; the per-channel gate (G = num_heads * head_dim) scales one
     channel each.
+
+Parity unpinned (no number on the pages fixes them; the tests pin every
+other property of these steps): the rotate-half pairing of ``rope`` as
+against an interleaved one, and which of the two head-gate widths the real
+afmoe model uses.
 """
 from __future__ import annotations
 
