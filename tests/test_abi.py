@@ -100,3 +100,13 @@ def test_create_rejects_null():
     assert lib.blk_forward(None, None, None, None, None) == L.BLK_E_NULL
     assert lib.blk_profile_end(None, 0, None, None, None) == -1
     lib.blk_destroy(None)  # ignored
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """With no built library the binding raises instead of falling back to
+    anything else."""
+    from transformer_decoder_block_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libblock.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load()
