@@ -135,11 +135,22 @@ def cpu_baseline(w, budget_s=12.0):
             R = min(w.S, R * 4)
         else:
             nb = min(w.B, nb * 2 if scale >= 2 else nb + 1)
+    # a whole workload that finishes in well under a second (the tiny
+    # shapes) is run again until the timing spans about a second
+    reps = 1
+    if dt < 1.0:
+        reps = int(min(1000, max(1, 1.0 / max(dt, 1e-4))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for b in range(nb):
+                ob.block_forward(x[b], None if mask is None else mask[b], W, cfg)
+        dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    tokens = R * nb
+    tokens = R * nb * reps
+    runs = f", {reps} runs" if reps > 1 else ""
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {R} tokens of {nb} of the {w.B} sequences ({w.name} shapes and "
-                      f"weights), fp64 NumPy, {dt:.2f} s"}
+                      f"weights), fp64 NumPy{runs}, {dt:.2f} s"}
 
 
 def main():

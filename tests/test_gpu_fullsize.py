@@ -69,18 +69,23 @@ def test_fullsize_stagewise(name):
         mid_tap = host(d["layer_mid"][b, rows])
         m_tap = host(d["mlp_input"][b, rows])
         lo_tap = host(d["layer_output"][b, rows])
-        assert rel_err(a_tap[rows], ob.rms_norm(x64[b, rows], W["w_in_norm"], w.eps)) <= BF16_BAR
+        stage = {}
+        stage["A"] = rel_err(a_tap[rows], ob.rms_norm(x64[b, rows], W["w_in_norm"], w.eps))
         att = ob.attention_sublayer(x64[b], a_tap, mk, W, cfg, rows)
-        assert rel_err(mid_tap, att["layer_mid"]) <= BF16_BAR
+        stage["C"] = rel_err(mid_tap, att["layer_mid"])
+        assert stage["A"] <= BF16_BAR and stage["C"] <= BF16_BAR, stage
         if "attention_scores" in d:
             sc = host(d["attention_scores"][b][:, torch.from_numpy(rows).cuda()])
             kmax = int(rows.max()) + 1
             check_scores(sc[:, :, :kmax], att["attention_scores"], BF16_BAR)
             assert np.all(np.isneginf(sc[:, :, kmax:]))
-        assert rel_err(m_tap, ob.mlp_norm(mid_tap, W, cfg)) <= BF16_BAR
+        stage["D"] = rel_err(m_tap, ob.mlp_norm(mid_tap, W, cfg))
         logits = host(d["router_logits"][b, rows]) if w.mlp == "moe" else None
         mo = ob.mlp_sublayer(mid_tap, m_tap, W, cfg, router_logits=logits)
-        assert rel_err(lo_tap, mo["layer_output"]) <= BF16_BAR
+        stage["E"] = rel_err(lo_tap, mo["layer_output"])
+        print(f"[fullsize] {name} b={b}: stage max|err|/RMS " +
+              " ".join(f"{k}={v:.4g}" for k, v in stage.items()), flush=True)
+        assert stage["D"] <= BF16_BAR and stage["E"] <= BF16_BAR, stage
         # end to end at the sampled rows, against the bf16 floor
         r = ob.block_forward(x64[b], mk, W, cfg, rows)
         emu = em.block_bf16(x64[b], mk, W, cfg, rows)
