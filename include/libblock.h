@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define BLK_ABI_VERSION 2
+#define BLK_ABI_VERSION 3
 
 typedef enum blk_status {
   BLK_OK = 0,
@@ -172,6 +172,10 @@ typedef struct blk_tap {
  *                                       (after the head gate)
  *  mlp_neurons           [B,S,I]        model dtype: the down projection's
  *                                       operand (SWIGLU, RELU2, XIELU)
+ *  mlp_activation        [B,S,I]        model dtype: the activation
+ *                                       function's output, silu(gate) on
+ *                                       SWIGLU (an extra GEMM), the neurons
+ *                                       on RELU2 and XIELU
  *  expert_outputs        [B,S,top_k,H]  model dtype: each slot's expert
  *                                       output times its weight (MOE)
  *  routed_output         [B,S,H]        F32: the sum of the slots (MOE)
@@ -202,6 +206,7 @@ typedef struct blk_taps {
   blk_tap expert_outputs;
   blk_tap routed_output;
   blk_tap shared_expert_output;
+  blk_tap mlp_activation;
 } blk_taps;
 
 /* The residual stream in and out. */

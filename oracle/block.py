@@ -302,15 +302,19 @@ def mlp_forward(m, W, cfg, router_logits=None):
     kind = cfg["mlp"]
     if kind == "swiglu":
         y, n = swiglu_mlp(m, W["w_gate"], W["w_up"], W["w_down"])
-        return {"mlp_raw": y, "mlp_neurons": n}
+        # [support] mlp_activation is act_fn's output: silu of the gate
+        # projection on a gated MLP
+        return {"mlp_raw": y, "mlp_neurons": n,
+                "mlp_activation": silu(linear(m, W["w_gate"]))}
     if kind == "relu2":
         y, n = relu2_mlp(m, W["w_up"], W["w_down"])
-        return {"mlp_raw": y, "mlp_neurons": n}
+        return {"mlp_raw": y, "mlp_neurons": n, "mlp_activation": n}
     if kind == "xielu":
         y, n = xielu_mlp(m, W["w_up"], W["w_down"], W["xielu_alpha_p"],
                          W["xielu_alpha_n"], cfg["xielu_beta"],
                          cfg["xielu_eps"])
-        return {"mlp_raw": y, "mlp_neurons": n}
+        # ungated: the activation is what the down projection receives
+        return {"mlp_raw": y, "mlp_neurons": n, "mlp_activation": n}
     if kind == "moe":
         return moe_mlp(m, W, cfg, router_logits)
     raise ValueError(kind)

@@ -1,6 +1,6 @@
 """GPU parity of the interior taps: the per-head queries, keys and values,
 the attention probabilities, the head outputs before and after the head
-gate, the MLP's neurons and the mixture's per-slot, routed and shared
+gate, the MLP's activation and neurons and the mixture's per-slot, routed and shared
 outputs, each against the fp64 oracle through the C ABI.
 
 Bars:
@@ -51,7 +51,7 @@ def interior_taps(w):
         if w.n_shared:
             t.append("shared_expert_output")
     else:
-        t.append("mlp_neurons")
+        t += ["mlp_neurons", "mlp_activation"]
     return t
 
 
@@ -88,6 +88,7 @@ def test_f32_interior_taps(w):
         check_probs(out["attention_probabilities"][b], r["attention_probabilities"])
         if w.mlp != "moe":
             assert rel_err(out["mlp_neurons"][b], r["mlp_neurons"]) <= F32_BAR
+            assert rel_err(out["mlp_activation"][b], r["mlp_activation"]) <= F32_BAR
             continue
         # a token whose choice differs at a float32 tie is left out (the
         # end-to-end test bounds how many there are)
@@ -144,10 +145,12 @@ def test_bf16_interior_taps_stagewise(w):
         m_tap = out["mlp_input"][b]
         if w.mlp != "moe":
             n_t = out["mlp_neurons"][b]
-            ref = ob.mlp_forward(m_tap, W, cfg)["mlp_neurons"]
+            mref = ob.mlp_forward(m_tap, W, cfg)
             # a product of two projections is heavy-tailed: the one bf16
-            # rounding of each neuron is checked elementwise
-            check_rounded(n_t, ref, 1)
+            # rounding of each neuron (and of each activation) is checked
+            # elementwise
+            check_rounded(n_t, mref["mlp_neurons"], 1)
+            check_rounded(out["mlp_activation"][b], mref["mlp_activation"], 1)
             mo = post_norm(ob.linear(n_t, W["w_down"]), W, cfg, "w_post_mlp_norm")
             assert rel_err(out["mlp_output"][b], mo) <= BF16_BAR
             continue

@@ -67,9 +67,10 @@ TAP_NAMES = ["layer_input", "attention_norm_output", "attention_scores",
              "mlp_output", "router_logits", "expert_indices", "expert_weights",
              "attention_queries", "attention_keys", "attention_values",
              "attention_probabilities", "attention_head_outputs", "attention_premix",
-             "mlp_neurons", "expert_outputs", "routed_output", "shared_expert_output"]
+             "mlp_neurons", "expert_outputs", "routed_output", "shared_expert_output",
+             "mlp_activation"]
 
-ABI_VERSION = 2  # the BLK_ABI_VERSION these structs mirror
+ABI_VERSION = 3  # the BLK_ABI_VERSION these structs mirror
 
 
 class blk_taps(C.Structure):

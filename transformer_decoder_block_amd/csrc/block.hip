@@ -327,6 +327,7 @@ blk_status check_taps(const blk_handle* h, const blk_taps* t) {
       {"attention_head_outputs", &t->attention_head_outputs, md, true},
       {"attention_premix", &t->attention_premix, md, true},
       {"mlp_neurons", &t->mlp_neurons, md, !moe},
+      {"mlp_activation", &t->mlp_activation, md, !moe},
       {"expert_outputs", &t->expert_outputs, md, moe},
       {"routed_output", &t->routed_output, BLK_F32, moe},
       {"shared_expert_output", &t->shared_expert_output, BLK_F32,
@@ -624,6 +625,24 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
       HIP_TRY(hipMemcpy2DAsync(tp.mlp_neurons.ptr, (size_t)I * es, h->neur,
                                neuron_ld(I) * es, (size_t)I * es, T, hipMemcpyDeviceToDevice, s),
               "neurons tap");
+    if (tp.mlp_activation.ptr) {
+      if (c.mlp_kind == BLK_MLP_SWIGLU) {
+        // act_fn's output is silu(gate), which the fused gate/up GEMM never
+        // stores: the gate projection again, with a silu epilogue
+        GemmParams a = p;
+        a.B[0] = w->w_gate;
+        a.nseg = 1;
+        a.seg_end[0] = I;
+        a.out = tp.mlp_activation.ptr;
+        a.ldo = I;
+        HIP_TRY(gemm(dt, EPI_SILU, a, T, s), "activation tap gemm");
+      } else {
+        HIP_TRY(hipMemcpy2DAsync(tp.mlp_activation.ptr, (size_t)I * es, h->neur,
+                                 neuron_ld(I) * es, (size_t)I * es, T,
+                                 hipMemcpyDeviceToDevice, s),
+                "activation tap");
+      }
+    }
 
     GemmParams d = gp0(h);
     d.M = T;

@@ -336,6 +336,8 @@ __device__ __forceinline__ void epi_quad(const GemmParams& p, int64_t orow, int 
         w[e] = rl * rl;
       } else if constexpr (EPI == EPI_XIELU) {
         w[e] = xielu_f(v[e], p.xa_p, p.xa_n, p.xbeta, p.xeps);
+      } else if constexpr (EPI == EPI_SILU) {
+        w[e] = silu_f(v[e]);
       } else {  // EPI_MOE_DOWN
         w[e] = wrow * v[e];
       }
@@ -1256,6 +1258,7 @@ static hipError_t dispatch_epi(EpiKind epi, bool grouped, const GemmParams& p,
     case EPI_SWIGLU: return launch<T, TL, EPI_SWIGLU, false>(p, max_rows, s);
     case EPI_RELU2: return launch<T, TL, EPI_RELU2, false>(p, max_rows, s);
     case EPI_XIELU: return launch<T, TL, EPI_XIELU, false>(p, max_rows, s);
+    case EPI_SILU: return launch<T, TL, EPI_SILU, false>(p, max_rows, s);
     case EPI_QKV:
       if constexpr (TL::FM <= 2 && TL::WN >= 128) {
         if (p.hd == 64) return launch<T, TL, EPI_QKV, false, 64>(p, max_rows, s);

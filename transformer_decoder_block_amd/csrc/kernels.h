@@ -20,7 +20,8 @@ enum EpiKind : int {
   EPI_RELU2 = 3,     // out = model(relu(acc)^2)
   EPI_XIELU = 4,     // out = model(xielu(acc))
   EPI_QKV = 5,       // q/k/v head-major scatter, q/k norm, rotary, gate
-  EPI_MOE_DOWN = 6   // out[row_pair[r]] = model(pair_weight[row_pair[r]] * acc)
+  EPI_MOE_DOWN = 6,  // out[row_pair[r]] = model(pair_weight[row_pair[r]] * acc)
+  EPI_SILU = 7       // out = model(silu(acc)): the gated MLP's activation tap
 };
 
 struct GemmParams {
