@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define BLK_ABI_VERSION 3
+#define BLK_ABI_VERSION 4
 
 typedef enum blk_status {
   BLK_OK = 0,
@@ -172,6 +172,10 @@ typedef struct blk_tap {
  *                                       (after the head gate)
  *  mlp_neurons           [B,S,I]        model dtype: the down projection's
  *                                       operand (SWIGLU, RELU2, XIELU)
+ *  mlp_norm_output       [B,S,H]        model dtype: the normed stream
+ *                                       entering the MLP (the same values
+ *                                       as mlp_input: the MLP is called
+ *                                       with the norm's output)
  *  mlp_activation        [B,S,I]        model dtype: the activation
  *                                       function's output, silu(gate) on
  *                                       SWIGLU (an extra GEMM), the neurons
@@ -207,6 +211,7 @@ typedef struct blk_taps {
   blk_tap routed_output;
   blk_tap shared_expert_output;
   blk_tap mlp_activation;
+  blk_tap mlp_norm_output;
 } blk_taps;
 
 /* The residual stream in and out. */

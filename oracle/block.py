@@ -445,8 +445,10 @@ def block_forward(x, key_mask, W, cfg, rows=None):
     mid = att["layer_mid"]
     m = mlp_norm(mid, W, cfg)
     mo = mlp_sublayer(mid, m, W, cfg)
+    # [support] mlp_norm_output is the norm's output and mlp_input what the
+    # MLP is called with: the same tensor in these blocks
     res = {"layer_input": x[rows], "attention_norm_output": a[rows],
-           "mlp_input": m}
+           "mlp_input": m, "mlp_norm_output": m}
     res.update(att)
     res.update(mo)
     return res

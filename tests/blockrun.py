@@ -81,6 +81,7 @@ class Run:
             "attention_premix": ((B, S, w.nh * w.hd), self.tdt, self.mdt),
             "mlp_neurons": ((B, S, w.I), self.tdt, self.mdt),
             "mlp_activation": ((B, S, w.I), self.tdt, self.mdt),
+            "mlp_norm_output": ((B, S, w.H), self.tdt, self.mdt),
             "expert_outputs": ((B, S, w.top_k, w.H), self.tdt, self.mdt),
             "routed_output": ((B, S, w.H), torch.float32, L.BLK_F32),
             "shared_expert_output": ((B, S, w.H), torch.float32, L.BLK_F32),

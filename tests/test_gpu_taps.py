@@ -43,8 +43,8 @@ ATTN_TAPS = ["attention_queries", "attention_keys", "attention_values",
 
 
 def interior_taps(w):
-    t = ["attention_norm_output", "layer_mid", "mlp_input", "attention_output",
-         "mlp_output"] + ATTN_TAPS
+    t = ["attention_norm_output", "layer_mid", "mlp_input", "mlp_norm_output",
+         "attention_output", "mlp_output"] + ATTN_TAPS
     if w.mlp == "moe":
         t += ["router_logits", "expert_indices", "expert_weights", "expert_outputs",
               "routed_output"]
@@ -79,9 +79,11 @@ def test_f32_interior_taps(w):
     run = Run(w)
     out = run.forward(interior_taps(w))
     x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    assert np.array_equal(out["mlp_norm_output"], out["mlp_input"])
     for b in range(w.B):
         mk = None if run.mask is None else run.mask[b]
         r = ob.block_forward(x64[b], mk, W, cfg)
+        assert rel_err(out["mlp_norm_output"][b], r["mlp_norm_output"]) <= F32_BAR
         for name in ("attention_queries", "attention_keys", "attention_values",
                      "attention_head_outputs", "attention_premix"):
             assert rel_err(out[name][b], r[name]) <= F32_BAR, name
@@ -108,6 +110,8 @@ def test_bf16_interior_taps_stagewise(w):
     x64, W, cfg = run.x64(), run.W64, w.as_dict()
     S, nh, hd = w.S, w.nh, w.hd
     pos = np.arange(S)
+    # the norm's output is the operand the MLP is called with
+    assert np.array_equal(out["mlp_norm_output"], out["mlp_input"])
     for b in range(w.B):
         mk = None if run.mask is None else run.mask[b]
         a_tap = out["attention_norm_output"][b]

@@ -68,9 +68,9 @@ TAP_NAMES = ["layer_input", "attention_norm_output", "attention_scores",
              "attention_queries", "attention_keys", "attention_values",
              "attention_probabilities", "attention_head_outputs", "attention_premix",
              "mlp_neurons", "expert_outputs", "routed_output", "shared_expert_output",
-             "mlp_activation"]
+             "mlp_activation", "mlp_norm_output"]
 
-ABI_VERSION = 3  # the BLK_ABI_VERSION these structs mirror
+ABI_VERSION = 4  # the BLK_ABI_VERSION these structs mirror
 
 
 class blk_taps(C.Structure):

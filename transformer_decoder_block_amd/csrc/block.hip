@@ -328,6 +328,7 @@ blk_status check_taps(const blk_handle* h, const blk_taps* t) {
       {"attention_premix", &t->attention_premix, md, true},
       {"mlp_neurons", &t->mlp_neurons, md, !moe},
       {"mlp_activation", &t->mlp_activation, md, !moe},
+      {"mlp_norm_output", &t->mlp_norm_output, md, true},
       {"expert_outputs", &t->expert_outputs, md, moe},
       {"routed_output", &t->routed_output, BLK_F32, moe},
       {"shared_expert_output", &t->shared_expert_output, BLK_F32,
@@ -583,6 +584,9 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
   if (tp.mlp_input.ptr)
     HIP_TRY(hipMemcpyAsync(tp.mlp_input.ptr, h->m, (size_t)T * H * es,
                            hipMemcpyDeviceToDevice, s), "mlp_input tap");
+  if (tp.mlp_norm_output.ptr)
+    HIP_TRY(hipMemcpyAsync(tp.mlp_norm_output.ptr, h->m, (size_t)T * H * es,
+                           hipMemcpyDeviceToDevice, s), "mlp_norm_output tap");
 
   // (5) MLP
   if (!moe) {
