@@ -11,6 +11,8 @@ C ABI, against the fp64 oracle (bars as in test_gpu_parity.py):
     than the sequence (identical to full causal);
   * exact ties among the router's biased scores (the lower expert index
     wins, slots in descending score order);
+  * a sliding window with 128-wide heads, and the float32 path at 2048
+    tokens and hidden 2048;
   * the widest hidden size the library accepts (8192) and the largest
     expert count (256).
 """
@@ -274,3 +276,30 @@ def test_persistent_grouped_gemm():
     w = afmoe("afmoe_pers", "bf16", B=1, S=512, E=8, top_k=8, I_e=2048, window=0,
               head_gate=0)
     check_bf16(Run(w))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_window_at_head_dim_128(dtype):
+    """A sliding window with 128-wide heads and grouped queries (the
+    windowed workloads use 64-wide heads): window edges fall inside key
+    tiles and inside a workgroup's query block."""
+    w = llama("llama_w_hd128", dtype, B=2, S=333, H=512, nh=4, nkv=2, hd=128, I=512,
+              window=100, seed=44)
+    CHECK[dtype](Run(w))
+
+
+def test_f32_at_larger_size():
+    """The float32 path beyond the small shapes: 2048 tokens, hidden 2048,
+    16 heads of 128 and MLP width 5504, end to end at the float32 bar on
+    sampled rows (first and last tokens, tile edges, random rows)."""
+    w = llama("llama_f32_big", "f32", B=1, S=2048, H=2048, nh=16, nkv=4, hd=128, I=5504,
+              seed=45)
+    run = Run(w)
+    out = run.forward(["layer_mid", "layer_output", "attention_norm_output"])
+    rows = np.array(sorted({0, 1, 63, 64, 127, 128, 1023, 1024, 2046, 2047} |
+                           set(np.random.default_rng(7).integers(0, 2048, 6).tolist())))
+    r = ob.block_forward(run.x64()[0], None, run.W64, w.as_dict(), rows)
+    assert rel_err(out["attention_norm_output"][0][rows], r["attention_norm_output"]) <= F32_BAR
+    assert rel_err(out["layer_mid"][0][rows], r["layer_mid"]) <= F32_BAR
+    assert rel_err(out["layer_output"][0][rows], r["layer_output"]) <= F32_BAR
+    assert rel_err(out["y"][0][rows], r["layer_output"]) <= F32_BAR
