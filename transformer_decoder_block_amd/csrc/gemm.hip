@@ -1187,14 +1187,14 @@ template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
 static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   const int n_per_tile = (EPI == EPI_SWIGLU) ? TL::BN / 2 : TL::BN;
   const int num_n = (p0.N + n_per_tile - 1) / n_per_tile;
-  if (GROUPED) {
+  constexpr bool PERSIST = TL::BM == 256 && TL::BN == 256 && TL::NS == 2 && TL::WGM == 2 &&
+                           sizeof(T) == 2 && EPI != EPI_QKV;
+  if (GROUPED && !PERSIST) {
     const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p0.ngroups;
     hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(max_tiles * num_n),
                        dim3(TL::NT), 0, s, p0);
     return hipGetLastError();
   }
-  constexpr bool PERSIST = TL::BM == 256 && TL::BN == 256 && TL::NS == 2 && TL::WGM == 2 &&
-                           sizeof(T) == 2 && EPI != EPI_QKV;
   if constexpr (PERSIST && GROUPED) {
     const int max_tiles = (max_rows + TL::BM - 1) / TL::BM + p0.ngroups;
     const int grid = std::min(max_tiles * num_n, cu_count());
