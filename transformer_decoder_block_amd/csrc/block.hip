@@ -48,7 +48,8 @@ struct blk_handle {
   float *gate = nullptr, *o = nullptr, *mid = nullptr, *mlp_raw = nullptr, *ew = nullptr,
         *rope_cos = nullptr, *rope_sin = nullptr;
   int *eidx = nullptr, *gcnt = nullptr, *goff = nullptr, *row_token = nullptr,
-      *row_pair = nullptr, *hist = nullptr;
+      *pair_row = nullptr, *hist = nullptr;
+  float* row_weight = nullptr;  // slot weight of each expert-ordered row
   // optional per-kernel event timing (blk_profile_begin / blk_profile_end)
   std::vector<hipEvent_t> pev;
   std::vector<const char*> pname;  // name of the span each mark opens
@@ -195,7 +196,8 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
     add((void**)&h->goff, E * 4);
     add((void**)&h->hist, (size_t)dispatch_hist_ints(T * kk, (int)E) * 4);
     add((void**)&h->row_token, T * kk * 4);
-    add((void**)&h->row_pair, T * kk * 4);
+    add((void**)&h->pair_row, T * kk * 4);
+    add((void**)&h->row_weight, T * kk * 4);
     add(&h->neur, T * kk * c.moe_intermediate * es);
     add(&h->stage, T * kk * H * es);
     if (c.num_shared_experts > 0) {
@@ -675,7 +677,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
       prof_mark(h, "gemm_down", s);
       HIP_TRY(gemm(dt, EPI_STORE, d, T, s), "mlp down gemm");
       prof_mark(h, "post_mlp_norm", s);
-      HIP_TRY(moe_combine(dt, nullptr, h->mlp_raw, h->mid, w->w_post_mlp_norm, 0,
+      HIP_TRY(moe_combine(dt, nullptr, nullptr, h->mlp_raw, h->mid, w->w_post_mlp_norm, 0,
                           (float*)tp.mlp_output.ptr, (float*)tp.layer_output.ptr, io->y, T,
                           H, eps, 1, s),
               "post-mlp norm");
@@ -720,8 +722,8 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     HIP_TRY(hipMemcpyAsync(tp.expert_weights.ptr, h->ew, (size_t)T * kk * 4,
                            hipMemcpyDeviceToDevice, s), "expert_weights tap");
   prof_mark(h, "dispatch", s);
-  HIP_TRY(moe_dispatch(h->eidx, T, kk, E, h->gcnt, h->goff, h->row_token, h->row_pair,
-                       h->hist, s),
+  HIP_TRY(moe_dispatch(h->eidx, h->ew, T, kk, E, h->gcnt, h->goff, h->row_token,
+                       h->pair_row, h->row_weight, h->hist, s),
           "dispatch");
   {
     GemmParams p = gp0(h);  // routed experts: gate/up + SwiGLU
@@ -748,7 +750,8 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     HIP_TRY(gemm(dt, EPI_SWIGLU, p, T * kk, s), "expert gate/up gemm");
   }
   {
-    GemmParams p = gp0(h);  // routed experts: down, scaled by the slot weight
+    GemmParams p = gp0(h);  // routed experts: down, scaled by the slot weight; the
+                            // rows stay in expert order (the combine gathers them)
     p.M = T * kk;
     p.N = H;
     p.K = Ie;
@@ -766,8 +769,7 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     p.b_group_stride = (int64_t)H * Ie;
     p.out = h->stage;
     p.ldo = H;
-    p.row_pair = h->row_pair;
-    p.pair_weight = h->ew;
+    p.row_weight = h->row_weight;
     prof_mark(h, "gemm_expert_down", s);
     HIP_TRY(gemm(dt, EPI_MOE_DOWN, p, T * kk, s), "expert down gemm");
   }
@@ -808,16 +810,17 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     HIP_TRY(gemm(dt, EPI_STORE, d, T, s), "shared down gemm");
   }
   if (tp.expert_outputs.ptr)
-    HIP_TRY(hipMemcpyAsync(tp.expert_outputs.ptr, h->stage, (size_t)T * kk * H * es,
-                           hipMemcpyDeviceToDevice, s), "expert outputs tap");
+    HIP_TRY(moe_gather_slots(dt, h->stage, h->pair_row, tp.expert_outputs.ptr, T * kk, H, s),
+            "expert outputs tap");
   if (tp.routed_output.ptr)
-    HIP_TRY(moe_sum_slots(dt, h->stage, kk, (float*)tp.routed_output.ptr, T, H, s),
+    HIP_TRY(moe_sum_slots(dt, h->stage, h->pair_row, kk, (float*)tp.routed_output.ptr, T, H,
+                          s),
             "routed output tap");
   if (tp.shared_expert_output.ptr)
     HIP_TRY(hipMemcpyAsync(tp.shared_expert_output.ptr, h->mlp_raw, (size_t)T * H * 4,
                            hipMemcpyDeviceToDevice, s), "shared expert output tap");
   prof_mark(h, "combine", s);
-  HIP_TRY(moe_combine(dt, h->stage, Ish > 0 ? h->mlp_raw : nullptr, h->mid,
+  HIP_TRY(moe_combine(dt, h->stage, h->pair_row, Ish > 0 ? h->mlp_raw : nullptr, h->mid,
                       w->w_post_mlp_norm, kk, (float*)tp.mlp_output.ptr,
                       (float*)tp.layer_output.ptr, io->y, T, H, eps, sandwich ? 1 : 0, s),
           "combine");

@@ -622,9 +622,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, ACC& acc, int
     return;
   } else {
     // The lane's rows: output offsets (and for the MoE down projection the
-    // slot's row and weight) are all loaded before the first store, so
-    // their latency is paid once.  Rows past the tile's end are clamped to
-    // a valid row for the loads and never stored.
+    // rows' slot weights) are all computed before the first store, so a
+    // load's latency is paid once.  Rows past the tile's end are clamped
+    // to a valid row for the loads and never stored.
     int64_t orow[AM];
     float wrow[AM];
     bool rok[AM];
@@ -635,14 +635,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, ACC& acc, int
       const int64_t row = row_begin + (rok[i] ? lr : 0);
       orow[i] = row * p.ldo;
       wrow[i] = 1.0f;
-      if constexpr (EPI == EPI_MOE_DOWN) orow[i] = p.row_pair[row];
-    }
-    if constexpr (EPI == EPI_MOE_DOWN) {
-#pragma unroll
-      for (int i = 0; i < AM; ++i) {
-        wrow[i] = p.pair_weight[orow[i]];
-        orow[i] *= p.ldo;
-      }
+      if constexpr (EPI == EPI_MOE_DOWN) wrow[i] = p.row_weight[row];
     }
     const int col0 = nt * BN + wn * WN;
     if (col0 + WN <= p.N) {

@@ -20,7 +20,7 @@ enum EpiKind : int {
   EPI_RELU2 = 3,     // out = model(relu(acc)^2)
   EPI_XIELU = 4,     // out = model(xielu(acc))
   EPI_QKV = 5,       // q/k/v head-major scatter, q/k norm, rotary, gate
-  EPI_MOE_DOWN = 6,  // out[row_pair[r]] = model(pair_weight[row_pair[r]] * acc)
+  EPI_MOE_DOWN = 6,  // out[r] = model(row_weight[r] * acc), rows in expert order
   EPI_SILU = 7       // out = model(silu(acc)): the gated MLP's activation tap
 };
 
@@ -56,8 +56,7 @@ struct GemmParams {
   // EPI_XIELU
   float xa_p, xa_n, xbeta, xeps;
   // EPI_MOE_DOWN
-  const int* row_pair;
-  const float* pair_weight;
+  const float* row_weight;  // the slot weight of each grouped row
   // EPI_QKV
   void* q; void* k; void* vt;   // [B,nh,S,hd], [B,nkv,S,hd], [B,nkv,hd,Sp]
                                 // with Sp = S rounded up to 64
@@ -92,14 +91,21 @@ hipError_t norm_add_norm(DType dt, const float* o, const void* x,
                          float* attn_out, float* mid, void* m, int rows,
                          int H, float eps, hipStream_t s);
 
-// MoE tail: raw = sum_k stage[t, k] + shared[t]; mo = norm_post(raw);
+// MoE tail.  stage holds the weighted expert outputs in expert order; the
+// output of slot s of token t is stage row pair_row[t*k + s].
+// raw = sum_k stage[pair_row[t, k]] + shared[t]; mo = norm_post(raw);
 // out = mid + mo -> out_f32 (may be null), y (model dtype).
-// routed[t] = sum over slots 0..k-1 (in that order) of stage[t*k + slot]
+// routed[t] = sum over slots 0..k-1 (in that order) of token t's slot rows
 // (the routed_output tap)
-hipError_t moe_sum_slots(DType dt, const void* stage, int top_k, float* routed, int rows,
-                         int H, hipStream_t s);
+hipError_t moe_sum_slots(DType dt, const void* stage, const int* pair_row, int top_k,
+                         float* routed, int rows, int H, hipStream_t s);
 
-hipError_t moe_combine(DType dt, const void* stage, const float* shared,
+// out[p] = stage[pair_row[p]] for the T*k (token, slot) pairs (the
+// expert_outputs tap, token-major)
+hipError_t moe_gather_slots(DType dt, const void* stage, const int* pair_row, void* out,
+                            int npairs, int H, hipStream_t s);
+
+hipError_t moe_combine(DType dt, const void* stage, const int* pair_row, const float* shared,
                        const float* mid, const void* g_post, int top_k,
                        float* mlp_out, float* out_f32, void* y, int rows,
                        int H, float eps, int sandwich, hipStream_t s);
@@ -130,11 +136,13 @@ hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T,
                     int E, int k, float route_scale, int* idx, float* w,
                     hipStream_t s);
 // Stable token-major dispatch of the T*k (token, slot) pairs by expert:
-// gcnt[E], goff[E], row_token[T*k], row_pair[T*k]; hist is scratch of
+// gcnt[E], goff[E]; for each grouped row r, row_token[r] (its token) and
+// row_weight[r] (its pair's slot weight w[pair]); for each pair p,
+// pair_row[p] (its grouped row).  hist is scratch of
 // dispatch_hist_ints(T*k, E) ints.
-hipError_t moe_dispatch(const int* idx, int T, int k, int E, int* gcnt,
-                        int* goff, int* row_token, int* row_pair, int* hist,
-                        hipStream_t s);
+hipError_t moe_dispatch(const int* idx, const float* w, int T, int k, int E, int* gcnt,
+                        int* goff, int* row_token, int* pair_row, float* row_weight,
+                        int* hist, hipStream_t s);
 constexpr int DISPATCH_CHUNK = 256;  // (token, slot) pairs per dispatch chunk
 inline int64_t dispatch_hist_ints(int64_t npairs, int E) {
   return ((npairs + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK) * E;

@@ -142,13 +142,15 @@ __global__ void __launch_bounds__(256) dispatch_scan(int* __restrict__ hist, int
 // among the chunk's earlier pairs of e.  The chunk is walked in rounds of
 // 64 consecutive pairs; a pair's rank inside its round is the number of
 // lower lanes holding the same expert.
-__global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx, int npairs,
+__global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx,
+                                                     const float* __restrict__ w, int npairs,
                                                      int k, int E, int nchunks,
                                                      const int* __restrict__ hist,
                                                      const int* __restrict__ gcnt,
                                                      int* __restrict__ goff,
                                                      int* __restrict__ row_token,
-                                                     int* __restrict__ row_pair) {
+                                                     int* __restrict__ pair_row,
+                                                     float* __restrict__ row_weight) {
   __shared__ int base[256];
   const int c = blockIdx.x, l = threadIdx.x;
   const int p0 = c * DCHUNK;
@@ -192,8 +194,9 @@ __global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx
     }
     if (ok) {
       const int pos = base[e] + rank;
-      row_pair[pos] = p0 + i;
+      pair_row[p0 + i] = pos;
       row_token[pos] = (p0 + i) / k;
+      row_weight[pos] = w[p0 + i];
     }
     __syncthreads();
     if (ok) atomicAdd(&base[e], 1);
@@ -201,15 +204,16 @@ __global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx
   }
 }
 
-hipError_t moe_dispatch(const int* idx, int T, int k, int E, int* gcnt, int* goff,
-                        int* row_token, int* row_pair, int* hist, hipStream_t s) {
+hipError_t moe_dispatch(const int* idx, const float* w, int T, int k, int E, int* gcnt,
+                        int* goff, int* row_token, int* pair_row, float* row_weight,
+                        int* hist, hipStream_t s) {
   const int npairs = T * k;
   const int nchunks = (npairs + DCHUNK - 1) / DCHUNK;
   hipLaunchKernelGGL(dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, npairs, E, nchunks,
                      hist);
   hipLaunchKernelGGL(dispatch_scan, dim3(E), dim3(256), 0, s, hist, nchunks, gcnt);
-  hipLaunchKernelGGL(dispatch_write, dim3(nchunks), dim3(64), 0, s, idx, npairs, k, E,
-                     nchunks, hist, gcnt, goff, row_token, row_pair);
+  hipLaunchKernelGGL(dispatch_write, dim3(nchunks), dim3(64), 0, s, idx, w, npairs, k, E,
+                     nchunks, hist, gcnt, goff, row_token, pair_row, row_weight);
   return hipGetLastError();
 }
 

@@ -136,13 +136,14 @@ struct Raw8<float> {
   }
 };
 
-// raw = shared[t] + the slots 0..k-1 in that order (stage[t*k + slot]).
-// The slot loads of a row go out several slots at a time for all of the
-// lane's chunks before any is added, so a wave keeps many loads in flight;
-// the sum order is fixed.
+// raw = shared[t] + the slots 0..k-1 in that order (slot s is stage row
+// pair_row[t*k + s]).  The slot loads of a row go out several slots at a
+// time for all of the lane's chunks before any is added, so a wave keeps
+// many loads in flight; the sum order is fixed.
 template <typename T, int MAXCH>
 __global__ void __launch_bounds__(256) moe_combine_kernel(
-    const T* __restrict__ stage, const float* __restrict__ shared,
+    const T* __restrict__ stage, const int* __restrict__ pair_row,
+    const float* __restrict__ shared,
     const float* __restrict__ mid, const T* __restrict__ g_post, int top_k,
     float* __restrict__ mlp_out, float* __restrict__ out_f32, T* __restrict__ y,
     int rows, int H, float eps, int sandwich) {
@@ -154,6 +155,8 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t base = (int64_t)row * H;
+  // lane s < top_k holds the stage row of slot s (top_k <= 64)
+  const int srow = lane < top_k ? pair_row[(int64_t)row * top_k + lane] : 0;
   float v[MAXCH][8], mv[PRE_MID ? MAXCH : 1][8];
 #pragma unroll
   for (int j = 0; j < MAXCH; ++j) {
@@ -170,13 +173,16 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(
   }
   for (int s0 = 0; s0 < top_k; s0 += SU) {
     Raw8<T> t[MAXCH][SU];
+    int64_t sb[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+      sb[u] = (int64_t)__builtin_amdgcn_readlane(srow, s0 + u < top_k ? s0 + u : 0) * H;
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j) {
       const int c = (lane + 64 * j) * 8;
 #pragma unroll
       for (int u = 0; u < SU; ++u)
-        if (c < H && s0 + u < top_k)
-          t[j][u].load(stage + ((int64_t)row * top_k + s0 + u) * H + c);
+        if (c < H && s0 + u < top_k) t[j][u].load(stage + sb[u] + c);
     }
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j) {
@@ -285,52 +291,76 @@ hipError_t norm_add_norm(DType dt, const float* o, const void* x, const void* g_
 }
 
 template <int MAXCH>
-static hipError_t comb_dispatch(DType dt, const void* stage, const float* shared,
+static hipError_t comb_dispatch(DType dt, const void* stage, const int* pair_row,
+                                const float* shared,
                                 const float* mid, const void* g_post, int top_k,
                                 float* mlp_out, float* out_f32, void* y, int rows, int H,
                                 float eps, int sandwich, hipStream_t s) {
   dim3 grid((rows + 3) / 4), block(256);
   if (dt == DType::BF16)
     hipLaunchKernelGGL((moe_combine_kernel<bf16, MAXCH>), grid, block, 0, s,
-                       (const bf16*)stage, shared, mid, (const bf16*)g_post, top_k,
+                       (const bf16*)stage, pair_row, shared, mid, (const bf16*)g_post, top_k,
                        mlp_out, out_f32, (bf16*)y, rows, H, eps, sandwich);
   else
     hipLaunchKernelGGL((moe_combine_kernel<float, MAXCH>), grid, block, 0, s,
-                       (const float*)stage, shared, mid, (const float*)g_post, top_k,
+                       (const float*)stage, pair_row, shared, mid, (const float*)g_post, top_k,
                        mlp_out, out_f32, (float*)y, rows, H, eps, sandwich);
   return hipGetLastError();
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) sum_slots_kernel(const T* __restrict__ stage, int top_k,
-                                                        float* __restrict__ routed, int rows,
-                                                        int H) {
+__global__ void __launch_bounds__(256) sum_slots_kernel(const T* __restrict__ stage,
+                                                        const int* __restrict__ pair_row,
+                                                        int top_k, float* __restrict__ routed,
+                                                        int rows, int H) {
   const int64_t n = (int64_t)rows * H;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / H, c = e % H;
     float acc = 0.f;
-    for (int s = 0; s < top_k; ++s) acc += to_f32(stage[(r * top_k + s) * H + c]);
+    for (int s = 0; s < top_k; ++s)
+      acc += to_f32(stage[(int64_t)pair_row[r * top_k + s] * H + c]);
     routed[e] = acc;
   }
 }
 
-hipError_t moe_sum_slots(DType dt, const void* stage, int top_k, float* routed, int rows,
-                         int H, hipStream_t s) {
+hipError_t moe_sum_slots(DType dt, const void* stage, const int* pair_row, int top_k,
+                         float* routed, int rows, int H, hipStream_t s) {
   const int64_t n = (int64_t)rows * H;
   const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
   if (dt == DType::BF16)
     hipLaunchKernelGGL((sum_slots_kernel<bf16>), dim3(blocks), dim3(256), 0, s,
-                       (const bf16*)stage, top_k, routed, rows, H);
+                       (const bf16*)stage, pair_row, top_k, routed, rows, H);
   else
     hipLaunchKernelGGL((sum_slots_kernel<float>), dim3(blocks), dim3(256), 0, s,
-                       (const float*)stage, top_k, routed, rows, H);
+                       (const float*)stage, pair_row, top_k, routed, rows, H);
   return hipGetLastError();
 }
 
-hipError_t moe_combine(DType dt, const void* stage, const float* shared, const float* mid,
-                       const void* g_post, int top_k, float* mlp_out, float* out_f32,
-                       void* y, int rows, int H, float eps, int sandwich, hipStream_t s) {
-#define C_(n) return comb_dispatch<n>(dt, stage, shared, mid, g_post, top_k, mlp_out, out_f32, y, rows, H, eps, sandwich, s)
+// One 256-thread block per (token, slot) pair: its stage row copied in
+// 4-byte words (H * sizeof(T) is a multiple of 16).
+__global__ void __launch_bounds__(256) gather_rows_kernel(const uint32_t* __restrict__ stage,
+                                                          const int* __restrict__ pair_row,
+                                                          uint32_t* __restrict__ out,
+                                                          int words) {
+  const int64_t p = blockIdx.x;
+  const uint32_t* src = stage + (int64_t)pair_row[p] * words;
+  uint32_t* dst = out + p * words;
+  for (int i = threadIdx.x; i < words; i += 256) dst[i] = src[i];
+}
+
+hipError_t moe_gather_slots(DType dt, const void* stage, const int* pair_row, void* out,
+                            int npairs, int H, hipStream_t s) {
+  const int words = H * (dt == DType::BF16 ? 2 : 4) / 4;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(npairs), dim3(256), 0, s,
+                     (const uint32_t*)stage, pair_row, (uint32_t*)out, words);
+  return hipGetLastError();
+}
+
+hipError_t moe_combine(DType dt, const void* stage, const int* pair_row, const float* shared,
+                       const float* mid, const void* g_post, int top_k, float* mlp_out,
+                       float* out_f32, void* y, int rows, int H, float eps, int sandwich,
+                       hipStream_t s) {
+#define C_(n) return comb_dispatch<n>(dt, stage, pair_row, shared, mid, g_post, top_k, mlp_out, out_f32, y, rows, H, eps, sandwich, s)
   BLK_BY_WIDTH(H, C_);
 #undef C_
 }
