@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define BLK_ABI_VERSION 4
+#define BLK_ABI_VERSION 5
 
 typedef enum blk_status {
   BLK_OK = 0,
@@ -247,6 +247,24 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out);
  */
 blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
                        const blk_taps* taps, void* stream);
+
+/*
+ * A stack of n_layers blocks of this handle's configuration, layers[0]
+ * first, each with its own weights: the model loop of the granite sheet
+ * "LlamaForCausalLM 32L-4096d", section "Implementing it", where each
+ * layer's output is the next layer's input.  io->x is the first layer's
+ * input and io->y receives the last layer's output; io->attention_mask
+ * (may be NULL) applies to every layer.  The outputs of the layers before
+ * the last alternate between io->y and a buffer of the handle's workspace
+ * (max_batch*max_seq*hidden in the model dtype), so nothing is allocated.
+ * Same contract as blk_forward, without taps; io and every layer's
+ * weights are validated before the first launch.  Errors: BLK_E_NULL,
+ * BLK_E_CONFIG (n_layers < 1, io.y aliasing io.x), BLK_E_SHAPE,
+ * BLK_E_ALIGN, BLK_E_HIP.
+ */
+blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
+                              const blk_weights* const* layers, int32_t n_layers,
+                              void* stream);
 
 /* Free the workspace and the handle (NULL is ignored). */
 void blk_destroy(blk_handle* h);

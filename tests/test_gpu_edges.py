@@ -260,6 +260,92 @@ def test_stack_of_blocks_on_one_handle():
         assert rel_err(host(y[b]), h2) <= F32_BAR
 
 
+def _layers_call(handle_run, runs, x, y, n=None):
+    """blk_forward_layers on handle_run's handle with the weights of runs."""
+    from transformer_decoder_block_amd import binding as L
+    w = handle_run.w
+    io = L.blk_io(x=x.data_ptr(), attention_mask=None, batch=w.B, seq=w.S, y=y.data_ptr())
+    layers = [r.block.w for r in runs]
+    st = L.blk_forward_layers(handle_run.block.h, io, layers,
+                              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return st
+
+
+def _one_by_one(handle_run, runs, x):
+    """The same stack as successive blk_forward calls on one handle."""
+    from transformer_decoder_block_amd import binding as L
+    w = handle_run.w
+    cur = x
+    for r in runs:
+        y = torch.empty_like(x)
+        io = L.blk_io(x=cur.data_ptr(), attention_mask=None, batch=w.B, seq=w.S,
+                      y=y.data_ptr())
+        st = L.blk_forward(handle_run.block.h, io, r.block.w, None,
+                           torch.cuda.current_stream().cuda_stream)
+        assert st == L.BLK_OK, L.blk_last_error()
+        cur = y
+    torch.cuda.synchronize()
+    return cur
+
+
+def test_forward_layers_f32_against_the_oracle_chain():
+    """Three blocks with their own weights in one call (the model loop):
+    the same bits as three blk_forward calls, and within the float32 bar of
+    the oracle applied layer after layer."""
+    from transformer_decoder_block_amd import binding as L
+    from tests.blockrun import host
+    w = llama("llama_layers", "f32", B=2, S=45, seed=60)
+    runs = [Run(w.replace(seed=60 + i)) for i in range(3)]
+    y = torch.empty_like(runs[0].xd)
+    assert _layers_call(runs[0], runs, runs[0].xd, y) == L.BLK_OK, L.blk_last_error()
+    assert torch.equal(y, _one_by_one(runs[0], runs, runs[0].xd))
+    cfg = w.as_dict()
+    for b in range(w.B):
+        h = runs[0].x64()[b]
+        for r in runs:
+            h = ob.block_forward(h, None, r.W64, cfg)["layer_output"]
+        assert rel_err(host(y[b]), h) <= F32_BAR
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_forward_layers_bf16_matches_single_calls(n):
+    """bf16 stacks of one and two layers (two: the first layer's output goes
+    through the handle's buffer) give the bits of successive blk_forward
+    calls, whose parity the other tests establish."""
+    from transformer_decoder_block_amd import binding as L
+    w = afmoe("afmoe_layers", "bf16", B=2, S=40, seed=61)
+    runs = [Run(w.replace(seed=61 + i)) for i in range(n)]
+    y = torch.empty_like(runs[0].xd)
+    assert _layers_call(runs[0], runs, runs[0].xd, y) == L.BLK_OK, L.blk_last_error()
+    assert torch.equal(y, _one_by_one(runs[0], runs, runs[0].xd))
+
+
+def test_forward_layers_errors_enqueue_nothing():
+    """n_layers < 1, a NULL layer, and a misaligned weight of a later layer
+    are refused before anything runs: y keeps its contents."""
+    import ctypes as C
+    from transformer_decoder_block_amd import binding as L
+    w = llama("llama_layers_err", "bf16", B=1, S=16, seed=62)
+    r0, r1 = Run(w), Run(w.replace(seed=63))
+    y = torch.full_like(r0.xd, 7.0)
+    io = L.blk_io(x=r0.xd.data_ptr(), attention_mask=None, batch=w.B, seq=w.S,
+                  y=y.data_ptr())
+    lib = L.load()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    arr = (C.POINTER(L.blk_weights) * 2)(C.pointer(r0.block.w), C.pointer(r1.block.w))
+    assert lib.blk_forward_layers(r0.block.h, C.byref(io), arr, 0, stream) == L.BLK_E_CONFIG
+    arr[1] = C.POINTER(L.blk_weights)()
+    assert lib.blk_forward_layers(r0.block.h, C.byref(io), arr, 2, stream) == L.BLK_E_NULL
+    bad = L.blk_weights()
+    C.memmove(C.addressof(bad), C.addressof(r1.block.w), C.sizeof(bad))
+    bad.wq = r1.block.w.wq + 2
+    arr[1] = C.pointer(bad)
+    assert lib.blk_forward_layers(r0.block.h, C.byref(io), arr, 2, stream) == L.BLK_E_ALIGN
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
 def test_persistent_gemm_single_stage_tiles():
     """The MLP up projection at 4096 tokens and width 2104 is 16 x 17 = 272
     tiles of 256 x 256 with a single K stage (hidden 64): the persistent

@@ -43,7 +43,8 @@ struct blk_handle {
   size_t ws_bytes = 0;
   // workspace views
   void *a = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *premix = nullptr,
-       *m = nullptr, *neur = nullptr, *logits = nullptr, *stage = nullptr, *nsh = nullptr;
+       *m = nullptr, *neur = nullptr, *logits = nullptr, *stage = nullptr, *nsh = nullptr,
+       *layer_out = nullptr;  // blk_forward_layers: outputs of the layers before the last
   float* split = nullptr;  // GEMM tail-split partial tiles
   float *gate = nullptr, *o = nullptr, *mid = nullptr, *mlp_raw = nullptr, *ew = nullptr,
         *rope_cos = nullptr, *rope_sin = nullptr;
@@ -184,6 +185,7 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
   if (c.sandwich_norm) add((void**)&h->o, T * H * 4);
   add((void**)&h->mid, T * H * 4);
   add(&h->m, T * H * es);
+  add(&h->layer_out, T * H * es);
   if (!moe) {
     add(&h->neur, T * neuron_ld(c.intermediate) * es);
     if (c.sandwich_norm) add((void**)&h->mlp_raw, T * H * 4);
@@ -826,5 +828,36 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
           "combine");
   prof_mark(h, "end", s);
   if (h->pmax) ++h->pfwd;
+  return BLK_OK;
+}
+
+extern "C" blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
+                                         const blk_weights* const* layers, int32_t n_layers,
+                                         void* stream) {
+  if (!h || !io || !layers) return fail(BLK_E_NULL, "handle, io and layers must not be NULL");
+  if (n_layers < 1) return fail(BLK_E_CONFIG, "n_layers must be >= 1");
+  if (!io->x || !io->y) return fail(BLK_E_NULL, "io.x and io.y must not be NULL");
+  if (io->x == io->y) return fail(BLK_E_CONFIG, "io.y must not alias io.x");
+  if (!aligned16(io->x) || !aligned16(io->y))
+    return fail(BLK_E_ALIGN, "io.x and io.y must be 16-byte aligned");
+  const blk_config& c = h->cfg;
+  if (io->batch < 1 || io->seq < 1 || io->batch > c.max_batch || io->seq > c.max_seq)
+    return fail(BLK_E_SHAPE, "batch/seq must be in [1, max_batch] x [1, max_seq]");
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (!layers[l]) return fail(BLK_E_NULL, "layer " + std::to_string(l) + " weights are NULL");
+    const blk_status st = check_weights(h, layers[l]);
+    if (st != BLK_OK) return st;
+  }
+  // layer l writes y when n_layers - 1 - l is even, else the workspace
+  // buffer, so the last layer writes y and no layer reads what it writes
+  const void* src = io->x;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    blk_io lio = *io;
+    lio.x = src;
+    lio.y = ((n_layers - 1 - l) % 2 == 0) ? io->y : h->layer_out;
+    const blk_status st = blk_forward(h, &lio, layers[l], nullptr, stream);
+    if (st != BLK_OK) return st;
+    src = lio.y;
+  }
   return BLK_OK;
 }
