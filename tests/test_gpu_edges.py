@@ -260,11 +260,17 @@ def test_stack_of_blocks_on_one_handle():
         assert rel_err(host(y[b]), h2) <= F32_BAR
 
 
-def _layers_call(handle_run, runs, x, y, n=None):
-    """blk_forward_layers on handle_run's handle with the weights of runs."""
+def _mask_ptr(run):
+    return None if run.maskd is None else run.maskd.data_ptr()
+
+
+def _layers_call(handle_run, runs, x, y):
+    """blk_forward_layers on handle_run's handle with the weights of runs
+    (and handle_run's padding mask, if any)."""
     from transformer_decoder_block_amd import binding as L
     w = handle_run.w
-    io = L.blk_io(x=x.data_ptr(), attention_mask=None, batch=w.B, seq=w.S, y=y.data_ptr())
+    io = L.blk_io(x=x.data_ptr(), attention_mask=_mask_ptr(handle_run), batch=w.B, seq=w.S,
+                  y=y.data_ptr())
     layers = [r.block.w for r in runs]
     st = L.blk_forward_layers(handle_run.block.h, io, layers,
                               torch.cuda.current_stream().cuda_stream)
@@ -279,8 +285,8 @@ def _one_by_one(handle_run, runs, x):
     cur = x
     for r in runs:
         y = torch.empty_like(x)
-        io = L.blk_io(x=cur.data_ptr(), attention_mask=None, batch=w.B, seq=w.S,
-                      y=y.data_ptr())
+        io = L.blk_io(x=cur.data_ptr(), attention_mask=_mask_ptr(handle_run), batch=w.B,
+                      seq=w.S, y=y.data_ptr())
         st = L.blk_forward(handle_run.block.h, io, r.block.w, None,
                            torch.cuda.current_stream().cuda_stream)
         assert st == L.BLK_OK, L.blk_last_error()
@@ -319,6 +325,27 @@ def test_forward_layers_bf16_matches_single_calls(n):
     y = torch.empty_like(runs[0].xd)
     assert _layers_call(runs[0], runs, runs[0].xd, y) == L.BLK_OK, L.blk_last_error()
     assert torch.equal(y, _one_by_one(runs[0], runs, runs[0].xd))
+
+
+def test_forward_layers_mask_applies_to_every_layer():
+    """A padded batch through a three-layer bf16 stack: the same bits as
+    three single calls with the same mask, and a stack with the mask
+    differs from one without it in the padded sequence only."""
+    from transformer_decoder_block_amd import binding as L
+    w = llama("llama_layers_pad", "bf16", B=2, S=48, pad=9, seed=64)
+    runs = [Run(w.replace(seed=64 + i)) for i in range(3)]
+    assert runs[0].maskd is not None
+    y = torch.empty_like(runs[0].xd)
+    assert _layers_call(runs[0], runs, runs[0].xd, y) == L.BLK_OK, L.blk_last_error()
+    assert torch.equal(y, _one_by_one(runs[0], runs, runs[0].xd))
+    # without the mask the unpadded first sequence is unchanged, the
+    # padded second one is not
+    saved, runs[0].maskd = runs[0].maskd, None
+    y_nomask = torch.empty_like(y)
+    assert _layers_call(runs[0], runs, runs[0].xd, y_nomask) == L.BLK_OK
+    runs[0].maskd = saved
+    assert torch.equal(y[0], y_nomask[0])
+    assert not torch.equal(y[1], y_nomask[1])
 
 
 def test_forward_layers_errors_enqueue_nothing():
