@@ -53,6 +53,10 @@ def test_fullsize_stagewise(name):
     # y is the bf16 rounding of the float32 layer_output, on every element
     assert torch.equal(d["layer_output"].to(torch.bfloat16).view(torch.int16),
                        d["y_raw"].view(torch.int16))
+    # the launch configuration bench.py times is deterministic: a second
+    # forward without taps gives the same bits
+    y2 = run.forward(on_device=True)["y_raw"]
+    assert torch.equal(y2.view(torch.int16), d["y_raw"].view(torch.int16))
     x64, W, cfg = run.x64(), run.W64, w.as_dict()
     rows = sample_rows(w)
     if w.mlp == "moe":

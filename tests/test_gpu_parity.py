@@ -176,7 +176,7 @@ def test_causality_bitwise(name):
     assert not torch.equal(y0[:, t0:], y1[:, t0:])
 
 
-@pytest.mark.parametrize("name", ["arcee_small", "afmoe_small"])
+@pytest.mark.parametrize("name", ["llama_small", "arcee_small", "afmoe_small"])
 def test_deterministic(name):
     w = synth.SMALL[name]
     run = Run(w)
