@@ -243,7 +243,9 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out);
  * at the caller's next synchronisation.  `taps` may be NULL.  Validation
  * (pointers, alignment, sizes, tap dtypes) happens before any launch.
  * A handle must not be used by two forwards that may run concurrently (the
- * workspace is shared).
+ * workspace is shared).  With taps NULL the call enqueues kernels only (no
+ * memset, copy or synchronisation), so it may be captured into a HIP graph
+ * and replayed while the pointers it was given stay valid.
  */
 blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
                        const blk_taps* taps, void* stream);
