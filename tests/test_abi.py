@@ -98,6 +98,7 @@ def test_create_rejects_null():
     assert lib.blk_create(None, None) == L.BLK_E_NULL
     assert "NULL" in L.blk_last_error()
     assert lib.blk_forward(None, None, None, None, None) == L.BLK_E_NULL
+    assert lib.blk_forward_layers(None, None, None, 1, None) == L.BLK_E_NULL
     assert lib.blk_profile_end(None, 0, None, None, None) == -1
     lib.blk_destroy(None)  # ignored
 
