@@ -176,6 +176,41 @@ def test_causality_bitwise(name):
     assert not torch.equal(y0[:, t0:], y1[:, t0:])
 
 
+def test_gqa_head_map_bitwise():
+    """An edit to KV head j (its rows of wk and wv) reaches exactly the query
+    heads g*j .. g*j+g-1: the other heads' outputs stay bit-identical."""
+    w = synth.SMALL["llama_small"]  # 6 query heads on 2 KV heads
+    g = w.nh // w.nkv
+    run = Run(w)
+    h0 = run.forward(["attention_head_outputs"], on_device=True)["attention_head_outputs"].clone()
+    j = 1
+    rows = slice(j * w.hd, (j + 1) * w.hd)
+    run.Wd["wk"][rows] *= 2
+    run.Wd["wv"][rows] *= 2
+    h1 = run.forward(["attention_head_outputs"], on_device=True)["attention_head_outputs"]
+    for h in range(w.nh):
+        same = torch.equal(h0[:, :, h], h1[:, :, h])
+        assert same == (h // g != j), h
+
+
+def test_expert_ablation_bitwise():
+    """Scaling expert e's down projection changes the output of exactly the
+    tokens that chose e; every other token stays bit-identical."""
+    w = synth.SMALL["afmoe_small"]
+    run = Run(w)
+    d0 = run.forward(["expert_indices"], on_device=True)
+    y0, idx = d0["y_raw"].clone(), d0["expert_indices"].clone()
+    e = 3
+    run.Wd["w_e_down"][e] *= 2
+    d1 = run.forward(["expert_indices"], on_device=True)
+    assert torch.equal(d1["expert_indices"], idx)  # the router did not move
+    chose = (idx == e).any(dim=-1)                 # [B, S]
+    assert chose.any() and (~chose).any()
+    diff = (d1["y_raw"] != y0).any(dim=-1)         # [B, S]
+    assert not diff[~chose].any()
+    assert diff[chose].float().mean() > 0.9
+
+
 @pytest.mark.parametrize("name", ["llama_small", "arcee_small", "afmoe_small"])
 def test_deterministic(name):
     w = synth.SMALL[name]
