@@ -373,6 +373,17 @@ def test_forward_layers_errors_enqueue_nothing():
     assert torch.all(y == 7.0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_grid_k_split(dtype):
+    """40 tokens, hidden 1024, MLP width 2000: o_proj, the up projection
+    (SwiGLU pairs in the fixup) and the down projection (ragged K = 2000)
+    each fill a handful of tiles with >= 16 K stages, so every tile runs as
+    several K parts added by the fixup in a fixed order."""
+    w = llama("llama_ksplit", dtype, B=1, S=40, H=1024, nh=8, nkv=2, hd=128, I=2000,
+              seed=45)
+    CHECK[dtype](Run(w))
+
+
 def test_persistent_gemm_single_stage_tiles():
     """The MLP up projection at 4096 tokens and width 2104 is 16 x 17 = 272
     tiles of 256 x 256 with a single K stage (hidden 64): the persistent

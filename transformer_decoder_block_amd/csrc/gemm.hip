@@ -712,7 +712,7 @@ gemm_kernel(const GemmParams p) {
 
   // ---- which tile
   int mt, nt, row_begin = 0, row_count = p.M, group = 0;
-  int split_slot = -1;  // >= 0: this block computes K half (split_slot & 1) of a tail tile
+  int split_slot = -1;  // >= 0: this block computes K part split_slot % split_parts of a split tile
   if constexpr (GROUPED) {
     // M tiles per group, exclusive prefix sums in LDS (the first wave: lane
     // j owns groups 4j .. 4j+3, at most 256 groups); the group of a tile is
@@ -763,13 +763,13 @@ gemm_kernel(const GemmParams p) {
     row_count = p.gcnt[lo];
   } else {
     const int num_m = (p.M + BM - 1) / BM;
-    // blocks [0, F) are whole tiles; with a tail split, blocks F + u are
-    // K half (u & 1) of tile F + u / 2 (dispatched last, spread over XCDs)
+    // blocks [0, F) are whole tiles; with a K split, blocks F + u are K
+    // part (u % split_parts) of tile F + u / split_parts (dispatched last)
     const int F = num_m * num_n - p.split_tiles;
     int id;
     if (p.split_tiles > 0 && (int)blockIdx.x >= F) {
       const int u = blockIdx.x - F;
-      id = F + u / 2;
+      id = F + u / p.split_parts;
       split_slot = u;
     } else {
       id = xcd_contiguous(blockIdx.x, p.split_tiles > 0 ? F : gridDim.x);
@@ -864,8 +864,11 @@ gemm_kernel(const GemmParams p) {
       for (int r = 0; r < 4 * QPB; ++r) acc[i][j][r] = 0.f;
 
   const int nk_all = (p.K + BK - 1) / BK;
-  const int k0 = split_slot >= 0 && (split_slot & 1) ? nk_all / 2 : 0;
-  const int nk = split_slot >= 0 ? ((split_slot & 1) ? nk_all - nk_all / 2 : nk_all / 2) : nk_all;
+  // K stages [k0, k0 + nk): all of them, or part q of S (S <= nk_all)
+  const int sp_q = split_slot >= 0 ? split_slot % p.split_parts : 0;
+  const int sp_n = split_slot >= 0 ? p.split_parts : 1;
+  const int k0 = sp_q * nk_all / sp_n;
+  const int nk = (sp_q + 1) * nk_all / sp_n - k0;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(k0 + st, st);
@@ -1119,10 +1122,10 @@ gemm_persistent_kernel(const GemmParams p) {
   }
 }
 
-// Tail-split fixup: split tile j is tile F + j of the grid (F = whole
-// tiles); its two K halves are float32 [BM][BN] tiles at split_ws[2j] and
-// split_ws[2j + 1].  Their sum (first half + second half) goes through the
-// same epilogue as a whole tile.
+// K-split fixup: split tile j is tile F + j of the grid (F = whole tiles);
+// its S = split_parts K parts are float32 [BM][BN] tiles at
+// split_ws[S j + q].  Their sum, added in part order, goes through the same
+// epilogue as a whole tile.
 template <typename T, int EPI, int BM, int BN, int WN>
 __global__ void __launch_bounds__(256) split_fixup_kernel(const GemmParams p) {
   constexpr bool PAIRED = (EPI == EPI_SWIGLU);
@@ -1132,31 +1135,34 @@ __global__ void __launch_bounds__(256) split_fixup_kernel(const GemmParams p) {
   const int j = blockIdx.x;
   int mt, nt;
   tile_coords(num_m * num_n - p.split_tiles + j, num_m, num_n, mt, nt);
-  const float* w0 = p.split_ws + (size_t)(2 * j) * BM * BN;
-  const float* w1 = w0 + (size_t)BM * BN;
+  const int S = p.split_parts;
+  const float* w0 = p.split_ws + (size_t)(S * j) * BM * BN;
+  auto sum4 = [&](int off, float (&v)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = w0[off + e];
+    for (int q = 1; q < S; ++q) {
+      const float* wq = w0 + (size_t)q * BM * BN + off;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += wq[e];
+    }
+  };
   for (int qd = threadIdx.x; qd < BM * BN / 4; qd += 256) {
     const int r = qd / (BN / 4), c = (qd % (BN / 4)) * 4;
     const int row = mt * BM + r;
     if (row >= p.M) continue;
-    const float* a0 = w0 + r * BN + c;
-    const float* a1 = w1 + r * BN + c;
     if constexpr (PAIRED) {
       const int cc = c % WN;
       if (cc >= WN / 2) continue;
       float g[4], u[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        g[e] = a0[e] + a1[e];
-        u[e] = a0[WN / 2 + e] + a1[WN / 2 + e];
-      }
+      sum4(r * BN + c, g);
+      sum4(r * BN + c + WN / 2, u);
       swiglu_quad<T>(p, (T*)p.out + (int64_t)row * p.ldo, nt * (BN / 2) + (c / WN) * (WN / 2) + cc,
                      g, u);
     } else {
       const int col = nt * BN + c;
       if (col >= p.N) continue;
       float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = a0[e] + a1[e];
+      sum4(r * BN + c, v);
       epi_quad<T, EPI>(p, (int64_t)row * p.ldo, col, v, 1.0f);
     }
   }
@@ -1197,18 +1203,35 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   }
   GemmParams p = p0;
   p.split_tiles = 0;
+  p.split_parts = 1;
   const int num_m = (p.M + TL::BM - 1) / TL::BM;
   const int tiles = num_m * num_n;
   if constexpr (EPI != EPI_QKV) {
-    // tail split: the last wave would leave more than half of the CUs idle.
-    // The partial tiles and the fixup cost a roughly fixed ~30 us, so only
-    // long K (>= 128 stages; measured: 288 stages gain 10%, 40 and 64 lose)
     const int cus = cu_count();
     const int rem = tiles % cus;
     const int nk = (p.K + TL::BK - 1) / TL::BK;
+    const size_t tile_bytes = (size_t)TL::BM * TL::BN * sizeof(float);
     if (tiles > cus && rem > 0 && rem <= cus / 2 && nk >= 128 && p.split_ws != nullptr &&
-        (size_t)rem * 2 * TL::BM * TL::BN * sizeof(float) <= p.split_ws_bytes)
+        (size_t)rem * 2 * tile_bytes <= p.split_ws_bytes) {
+      // tail split: the last wave would leave more than half of the CUs
+      // idle.  The partial tiles and the fixup cost a roughly fixed ~30 us,
+      // so only long K (>= 128 stages; measured: 288 stages gain 10%, 40
+      // and 64 lose)
       p.split_tiles = rem;
+      p.split_parts = 2;
+    } else if (4 * tiles <= cus && nk >= 16 && p.split_ws != nullptr) {
+      // a grid on at most a quarter of the CUs: every tile in S K parts of
+      // at least 4 stages, so that the grid's stage-by-stage latency is
+      // paid on S times fewer stages (measured on the tiny float32 block:
+      // 22 stages in 5 parts 52 -> 29 us; 8 stages in 2 parts gain or lose
+      // about 2 us, so shorter K stays whole)
+      int S = std::min(std::min(nk / 4, cus / tiles), 16);
+      while (S >= 2 && (size_t)tiles * S * tile_bytes > p.split_ws_bytes) --S;
+      if (S >= 2) {
+        p.split_tiles = tiles;
+        p.split_parts = S;
+      }
+    }
   }
   if constexpr (PERSIST && !GROUPED) {
     if (p.split_tiles == 0) {
@@ -1217,8 +1240,8 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(tiles + p.split_tiles),
-                     dim3(TL::NT), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>),
+                     dim3(tiles + p.split_tiles * (p.split_parts - 1)), dim3(TL::NT), 0, s, p);
   if constexpr (EPI != EPI_QKV) {
     if (p.split_tiles > 0)
       hipLaunchKernelGGL((split_fixup_kernel<T, EPI, TL::BM, TL::BN, TL::WN>),

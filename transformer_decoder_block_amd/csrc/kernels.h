@@ -66,14 +66,15 @@ struct GemmParams {
   const void* q_norm_w; const void* k_norm_w;
   const float* rope_cos; const float* rope_sin;   // [S_max, hd/2]
   float eps;
-  // Tail split (chosen by gemm(); the caller only provides the scratch):
-  // when the last wave of tiles would leave more than half of the CUs idle,
-  // its split_tiles tiles are computed as two K halves whose float32
-  // partial tiles go to split_ws; a fixup kernel adds the halves in a fixed
-  // order and applies the epilogue.
+  // K split (chosen by gemm(); the caller only provides the scratch): the
+  // last split_tiles tiles of the grid are each computed as split_parts K
+  // ranges whose float32 partial tiles go to split_ws; a fixup kernel adds
+  // the parts in a fixed order and applies the epilogue.  Used for the
+  // tail of a large grid (two parts) and for grids that fill few CUs.
   float* split_ws;
   size_t split_ws_bytes;
   int split_tiles;
+  int split_parts;
 };
 
 hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
