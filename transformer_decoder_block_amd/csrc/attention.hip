@@ -55,6 +55,25 @@ __device__ __forceinline__ int xcd_contiguous_a(int bid, int nblk) {
                      : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Work id of a block.  Ids are group-major, ((b * nkv + KV head) * nqb +
+// qbr) * g + head of the group, where qbr = 0 is the last (heaviest) query
+// block under the causal mask.  Each XCD receives a contiguous range of ids.
+// When the (b, KV head) groups divide evenly over the 8 XCDs, that range is
+// whole groups, and its blocks are dealt heaviest query block first across
+// all of them, a longest-first list schedule; the query heads of one KV head
+// stay consecutive, so they stream the same K/V tiles together.  Otherwise
+// the heavy-first order holds within each group.
+__device__ __forceinline__ int attn_work_id(int bid, int nblk, int ngroups, int g, int nqb) {
+  int id = xcd_contiguous_a(bid, nblk);
+  if (ngroups % 8 == 0) {
+    const int gx = ngroups / 8, per = gx * g * nqb;
+    const int x = id / per, l = id - x * per;
+    const int qbr = l / (gx * g), r = l - qbr * (gx * g);
+    id = x * per + ((r / g) * nqb + qbr) * g + r % g;
+  }
+  return id;
+}
+
 // element offset of 16-byte chunk c of row r in a swizzled tile whose rows
 // hold CPR chunks
 template <typename T, int CPR>
@@ -87,7 +106,7 @@ attn_kernel(const AttnParams p) {
   const int nqb = (p.S + QB - 1) / QB;
 
   // ---- which (b, head, query block)
-  const int id = xcd_contiguous_a(blockIdx.x, gridDim.x);
+  const int id = attn_work_id(blockIdx.x, gridDim.x, p.B * p.nkv, g, nqb);
   const int hg = id % g;
   const int qbr = (id / g) % nqb;
   const int kvh = (id / (g * nqb)) % p.nkv;
@@ -425,7 +444,7 @@ attn_bf16_kernel(const AttnParams p) {
   const int nqb = (p.S + BQB - 1) / BQB;
 
   // ---- which (b, KV head, query block, head of the group)
-  const int id = xcd_contiguous_a(blockIdx.x, gridDim.x);
+  const int id = attn_work_id(blockIdx.x, gridDim.x, p.B * p.nkv, g, nqb);
   const int hg = id % g;
   const int qbr = (id / g) % nqb;
   const int kvh = (id / (g * nqb)) % p.nkv;
