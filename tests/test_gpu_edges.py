@@ -114,6 +114,19 @@ def test_short_and_ragged_sequences(dtype, S):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,nh,nkv,hd", [(1, 8, 8, 64), (2, 8, 8, 128), (3, 16, 8, 64),
+                                         (2, 6, 3, 64)])
+def test_attention_block_order(dtype, B, nh, nkv, hd):
+    """The attention launch deals the blocks of an XCD heaviest query block
+    first across its (batch, KV head) groups when the groups divide over the
+    8 XCDs (8, 16 and 24 groups here, one or two query heads each), and per
+    group otherwise (6 groups).  A mapping that ran a block twice or not at
+    all would leave rows wrong: every row of every tap is checked."""
+    CHECK[dtype](Run(llama(f"llama_order_{B}_{nh}_{nkv}_{hd}", dtype, B=B, S=300, nh=nh,
+                           nkv=nkv, hd=hd, seed=44)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_token_moe(dtype):
     CHECK[dtype](Run(afmoe("afmoe_s1", dtype, B=3, S=1)))
 
