@@ -22,9 +22,9 @@ import torch
 
 from oracle import block as ob
 from transformer_decoder_block_amd import synth
-from tests import bf16_emulation as em
+from oracle import bf16_emulation as em
 from tests.blockrun import Run, dev, rel_err
-from tests.test_gpu_parity import BF16_BAR, F32_BAR, check_scores, floor_bar, near_tie
+from tests.test_gpu_parity import BF16_BAR, F32_BAR, check_floor, check_scores, near_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -90,7 +90,8 @@ def check_bf16(run, mask=None):
         assert rel_err(out["layer_mid"][b], att["layer_mid"]) <= BF16_BAR
         fl = rel_err(em.attention_sublayer_bf16(x64[b], a_tap, mk, W, cfg)["attention_output"],
                      att["attention_output"])
-        assert rel_err(out["attention_output"][b], att["attention_output"]) <= floor_bar(fl)
+        check_floor(f"{w.name} b={b}", "attention_output",
+                    rel_err(out["attention_output"][b], att["attention_output"]), fl)
         mid_tap, m_tap = out["layer_mid"][b], out["mlp_input"][b]
         assert rel_err(m_tap, ob.mlp_norm(mid_tap, W, cfg)) <= BF16_BAR
         logits = None
@@ -222,20 +223,36 @@ def test_most_experts(dtype):
 def test_split_tail_tiles():
     """o_proj at 4352 tokens x 4096 outputs, K = 64 heads x 128 = 8192, is
     272 tiles of 256 x 256 with 128 K stages on a 256-CU part: its last 16
-    tiles (rows 4096-4351) run as two K halves summed by the fixup.  Their
-    rows of layer_mid match the oracle like any other row, and y is still
-    the rounding of the float32 layer_output."""
+    tiles (rows 4096-4351) run as two K halves summed by the fixup.  Every
+    row of those tiles, and rows of the whole tiles around them, match the
+    oracle on layer_mid, and y is still the rounding of the float32
+    layer_output.  The Q/K/V GEMM of this shape (17 x 40 tiles) runs the
+    large Q/K/V tile: its queries, keys and values are checked on every
+    element."""
+    from tests.blockrun import host
+    from tests.test_gpu_tileq import check_rounded
     w = llama("llama_split", "bf16", B=1, S=4352, H=4096, nh=64, nkv=8, hd=128, I=512)
     run = Run(w)
-    d = run.forward(["attention_norm_output", "layer_mid", "layer_output"], on_device=True)
+    d = run.forward(["attention_norm_output", "layer_mid", "layer_output",
+                     "attention_queries", "attention_keys", "attention_values"],
+                    on_device=True)
     lo = d["layer_output"].to(torch.bfloat16).view(torch.int16)
     assert torch.equal(lo, d["y_raw"].view(torch.int16))
-    from tests.blockrun import host
-    rows = np.array([0, 1, 2047, 4095, 4096, 4097, 4200, 4350, 4351])
     x64, W, cfg = run.x64(), run.W64, w.as_dict()
     a_tap = host(d["attention_norm_output"][0])
-    att = ob.attention_sublayer(x64[0], a_tap, None, W, cfg, rows)
-    assert rel_err(host(d["layer_mid"][0][torch.from_numpy(rows).cuda()]), att["layer_mid"]) <= BF16_BAR
+    # q, k, v of every token from the GPU's normed stream
+    q, k, v = ob.qkv_heads(a_tap, W, cfg, np.arange(w.S))
+    check_rounded(host(d["attention_queries"][0]), q)
+    check_rounded(host(d["attention_keys"][0]), k)
+    check_rounded(host(d["attention_values"][0]), v)
+    del q, k, v
+    # every row of the split tiles, plus rows of whole tiles
+    rows = np.concatenate([np.array([0, 1, 255, 256, 2047, 3839, 4094, 4095]),
+                           np.arange(4096, 4352)])
+    mid = host(d["layer_mid"][0][torch.from_numpy(rows).cuda()])
+    for part in np.array_split(np.arange(len(rows)), 4):
+        att = ob.attention_sublayer(x64[0], a_tap, None, W, cfg, rows[part])
+        assert rel_err(mid[part], att["layer_mid"]) <= BF16_BAR
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -13,19 +13,26 @@ Bars (written here, derived in the design notes):
     own RMS is far below the stream's) and the end-to-end error from
     layer_input alone are judged against the bf16 floor: the same
     computation in float64 rounded to bf16 exactly where a bf16-operand
-    path must round (tests/bf16_emulation.py).  Bar: max(2e-2, 1.5 x that
-    floor); the factor covers the different (but equally sized) rounding
-    sample that fp32 accumulation and the online softmax draw.
+    path must round (oracle/bf16_emulation.py).  Bar: max(2e-2, factor x
+    that floor).  The factor of each value is the largest ratio to the
+    floor that independent dithered-rounding samples of the same bf16 path
+    reach (tests/golden/floor_factor.py writes them into
+    tests/golden/floor_factor.json): a GPU that rounds at the same points
+    draws another such sample.  Every gated comparison prints its
+    GPU / floor ratio.
 The small workloads span several GEMM / attention tiles and end in ragged
 tails; every token of every sequence is compared.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 from oracle import block as ob
 from transformer_decoder_block_amd import synth
-from tests import bf16_emulation as em
+from oracle import bf16_emulation as em
 from tests.blockrun import Run, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -40,11 +47,21 @@ MOE_TAPS = ["router_logits", "expert_indices", "expert_weights"]
 
 F32_BAR = 1e-4
 BF16_BAR = 2e-2
-FLOOR_FACTOR = 1.5
+with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                       "floor_factor.json")) as _fh:
+    FLOOR_FACTOR = json.load(_fh)["floor_factor"]
 
 
-def floor_bar(floor):
-    return max(BF16_BAR, FLOOR_FACTOR * floor)
+def floor_bar(floor, value="end_to_end_y"):
+    return max(BF16_BAR, FLOOR_FACTOR[value] * floor)
+
+
+def check_floor(tag, value, got, floor):
+    """got <= max(2e-2, factor x floor), printing the GPU / floor ratio."""
+    bar = floor_bar(floor, value)
+    print(f"[floor] {tag} {value}: gpu {got:.4g} floor {floor:.4g} ratio "
+          f"{got / floor:.3f} (factor {FLOOR_FACTOR[value]}, bar {bar:.4g})", flush=True)
+    assert got <= bar, (tag, value, got, floor)
 
 
 def taps_for(w):
@@ -111,7 +128,6 @@ def test_bf16_stagewise(w):
     # y is the bf16 rounding (nearest even) of the float32 layer_output tap
     lo = torch.from_numpy(out["layer_output"].astype(np.float32)).to(torch.bfloat16)
     assert torch.equal(lo.view(torch.int16), out["y_raw"].cpu().view(torch.int16))
-    e2e = []
     for b in range(w.B):
         mk = None if run.mask is None else run.mask[b]
         a_tap = out["attention_norm_output"][b]
@@ -123,7 +139,8 @@ def test_bf16_stagewise(w):
         assert rel_err(out["layer_mid"][b], att["layer_mid"]) <= BF16_BAR
         fl = rel_err(em.attention_sublayer_bf16(x64[b], a_tap, mk, W, cfg)
                      ["attention_output"], att["attention_output"])
-        assert rel_err(out["attention_output"][b], att["attention_output"]) <= floor_bar(fl)
+        check_floor(f"{w.name} b={b}", "attention_output",
+                    rel_err(out["attention_output"][b], att["attention_output"]), fl)
         # stage D: MLP-input norm from the GPU's float32 layer_mid
         mid_tap = out["layer_mid"][b]
         assert rel_err(out["mlp_input"][b], ob.mlp_norm(mid_tap, W, cfg)) <= BF16_BAR
@@ -143,7 +160,8 @@ def test_bf16_stagewise(w):
         mo = ob.mlp_sublayer(mid_tap, m_tap, W, cfg, router_logits=logits)
         fl = rel_err(em.mlp_sublayer_bf16(mid_tap, m_tap, W, cfg, logits)["mlp_output"],
                      mo["mlp_output"])
-        assert rel_err(out["mlp_output"][b], mo["mlp_output"]) <= floor_bar(fl)
+        check_floor(f"{w.name} b={b}", "mlp_output",
+                    rel_err(out["mlp_output"][b], mo["mlp_output"]), fl)
         assert rel_err(out["layer_output"][b], mo["layer_output"]) <= BF16_BAR
         # end to end from layer_input alone, against the bf16 floor
         r = ob.block_forward(x64[b], mk, W, cfg)
@@ -157,9 +175,7 @@ def test_bf16_stagewise(w):
             assert same.mean() > 0.9
         got = rel_err(out["y"][b][same], r["layer_output"][same])
         floor = rel_err(ob.round_bf16(emu["layer_output"][same]), r["layer_output"][same])
-        e2e.append((got, floor))
-        assert got <= floor_bar(floor), (got, floor)
-    print(f"{w.name}: end-to-end y max|err|/RMS (gpu, bf16 floor) = {e2e}")
+        check_floor(f"{w.name} b={b}", "end_to_end_y", got, floor)
 
 
 @pytest.mark.parametrize("name", ["llama_small", "afmoe_small"])
