@@ -145,18 +145,33 @@ def cpu_baseline(w, budget_s=12.0):
             for b in range(nb):
                 ob.block_forward(x[b], None if mask is None else mask[b], W, cfg)
         dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                             for i in info if i.get("user_api") == "blas"})) or "unknown"
     tokens = R * nb * reps
     runs = f", {reps} runs" if reps > 1 else ""
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {R} tokens of {nb} of the {w.B} sequences ({w.name} shapes and "
-                      f"weights), fp64 NumPy{runs}, {dt:.2f} s"}
+                      f"weights), fp64 NumPy{runs}, {dt:.2f} s",
+            "cpu_model": cpu_model(), "blas": blas}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,15 +213,21 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K steps on one stream, per-kernel events recorded inside
+    # by the library, plus one event pair per step on the same stream
     L.blk_profile_begin(blk.h, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i][0].record(stream)
         blk.forward(x, y, maskd, stream=stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     prof = L.blk_profile_end(blk.h) or []
     ms_step = wall * 1e3 / args.steps
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -246,8 +267,18 @@ def main():
                    "heads": w.nh, "kv_heads": w.nkv, "head_dim": w.hd,
                    "mlp": w.mlp, "intermediate": w.I or w.I_e,
                    "parallelism": "none (1 GPU)"},
+        # per-step device time (HIP events on the stream, K steps)
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p10": round(float(np.quantile(step_ms, 0.1)), 4),
+                    "p90": round(float(np.quantile(step_ms, 0.9)), 4),
+                    "n": int(len(step_ms))},
+        # the whole block's algorithmic FLOP rate and its share of the
+        # dense MFMA peak (the metric's "% MFMA peak"); roofline below is
+        # the dominant kernel alone
         "block_tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
         "block_frac_of_peak": round(flops / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "block_frac_of_peak_median_step": round(
+            flops / (float(np.median(step_ms)) * 1e-3) / 1e12 / peak, 4),
         "gflop_per_step": round(flops / 1e9, 1),
         "roofline": roof,
         "kernels": per_kernel,

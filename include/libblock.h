@@ -27,8 +27,10 @@
  *  - Model-dtype tensors (x, y, weights, operand taps) are BLK_F32 (IEEE
  *    float) or BLK_BF16 (bfloat16 bit patterns) as set by blk_config.dtype.
  *  - Errors are returned as blk_status; no exception crosses the ABI.  A
- *    failed call enqueues nothing.  blk_last_error() gives a readable
- *    reason for the calling thread's last failure.
+ *    call refused by validation enqueues nothing; a BLK_E_HIP from a
+ *    forward leaves the launches before the failing one enqueued (see
+ *    blk_forward).  blk_last_error() gives a readable reason for the
+ *    calling thread's last failure.
  *  - Results are bitwise deterministic for identical inputs (no floating
  *    point atomics anywhere).
  */
@@ -241,7 +243,13 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out);
  * the default stream) and return.  No host synchronisation, no allocation,
  * no weight copies.  Success means "enqueued"; device-side faults surface
  * at the caller's next synchronisation.  `taps` may be NULL.  Validation
- * (pointers, alignment, sizes, tap dtypes) happens before any launch.
+ * (pointers, alignment, sizes, tap dtypes) happens before any launch, so a
+ * validation error (BLK_E_NULL, BLK_E_CONFIG, BLK_E_SHAPE, BLK_E_ALIGN,
+ * BLK_E_DTYPE) enqueues nothing and leaves y untouched.  BLK_E_HIP is
+ * different: it reports a launch (or tap copy) that the HIP runtime refused
+ * part-way through the sequence, and the kernels enqueued before it stay
+ * enqueued and run; y and the taps are then undefined, the handle stays
+ * usable, and blk_last_error() names the step that failed.
  * A handle must not be used by two forwards that may run concurrently (the
  * workspace is shared).  With taps NULL the call enqueues kernels only (no
  * memset, copy or synchronisation), so it may be captured into a HIP graph
@@ -260,9 +268,11 @@ blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
  * the last alternate between io->y and a buffer of the handle's workspace
  * (max_batch*max_seq*hidden in the model dtype), so nothing is allocated.
  * Same contract as blk_forward, without taps; io and every layer's
- * weights are validated before the first launch.  Errors: BLK_E_NULL,
- * BLK_E_CONFIG (n_layers < 1, io.y aliasing io.x), BLK_E_SHAPE,
- * BLK_E_ALIGN, BLK_E_HIP.
+ * weights are validated before the first launch, so a validation error
+ * enqueues nothing.  A BLK_E_HIP in layer l leaves layers 0 .. l-1 and the
+ * kernels of layer l before the failing one enqueued; y is then undefined.
+ * Errors: BLK_E_NULL, BLK_E_CONFIG (n_layers < 1, io.y aliasing io.x),
+ * BLK_E_SHAPE, BLK_E_ALIGN, BLK_E_HIP.
  */
 blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
                               const blk_weights* const* layers, int32_t n_layers,

@@ -57,9 +57,10 @@ F64 = np.float64
 def rms_norm(x, g, eps):
     """RMSNorm over the last axis: g * x / sqrt(mean(x^2) + eps).
 
-    [llama] ``rmsnorm(x, layers[i].input_layernorm, eps=1e-05)``; [afmoe]
-    notes that RMSNorm is scale-invariant up to eps.  The formula itself is
-    not printed; this is the reading stated in the module docstring.
+    [llama] applies the layer's input norm with eps 1e-5 but prints no
+    formula; [afmoe] section 03 remarks that the norm ignores the scale of
+    its input (up to eps).  This is the reading stated in the module
+    docstring.
     """
     x = np.asarray(x, F64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
@@ -69,8 +70,9 @@ def rms_norm(x, g, eps):
 def linear(x, w):
     """A bias-free Linear: x @ w.T with w in [out_features, in_features].
 
-    [llama] ``h @ layers[i].self_attn.q_proj.T``; the printouts show every
-    projection as ``Linear(..., bias=False)``.
+    [llama] multiplies the stream by the transposed projection matrices;
+    the module printouts of the nnterp pages list every projection without
+    a bias.
     """
     return np.asarray(x, F64) @ np.asarray(w, F64).T
 
@@ -78,8 +80,8 @@ def linear(x, w):
 def rope_cos_sin(positions, hd, theta):
     """Angles of the plain rotary embedding: phi[s, i] = s * theta^(-2i/hd).
 
-    [llama] ``q, k = rope(q, k, theta=10000)``.  Returns cos, sin of shape
-    [len(positions), hd/2].
+    [llama] rotates q and k with base 10000 after the projections.  Returns
+    cos, sin of shape [len(positions), hd/2].
     """
     i = np.arange(hd // 2, dtype=F64)
     inv_freq = theta ** (-2.0 * i / hd)
@@ -101,10 +103,10 @@ def rope(u, cos, sin):
 def visibility(q_pos, k_pos, key_mask, window):
     """Boolean [len(q_pos), len(k_pos)]: may query q_pos[a] read key k_pos[b]?
 
-    Causal ([llama] ``mask=causal``), restricted to real keys (the [support]
-    tables: attention_mask zeros are padding) and, when window > 0, to the
-    last ``window`` positions including the query's own ([afmoe] "attend over
-    the last sliding_window tokens").
+    Causal ([llama] masks the softmax causally), restricted to real keys
+    (the [support] tables mark padding with zeros in attention_mask) and,
+    when window > 0, to the ``window`` most recent positions, the query's
+    own included ([afmoe] section 03 on the sliding-window blocks).
     """
     qp = np.asarray(q_pos)[:, None]
     kp = np.asarray(k_pos)[None, :]
@@ -134,9 +136,10 @@ def attention(q, k, v, q_pos, k_pos, key_mask, window):
     """Grouped-query softmax attention for one sequence.
 
     q [nh, Sq, hd], k [nkv, Sk, hd], v [nkv, Sk, hd].  Query head h reads
-    KV head h // (nh // nkv): the arcee page's "an edit to key/value head j
-    reaches query heads 5j to 5j + 4" (and the apertus page's 4j .. 4j+3).
-    [llama] ``softmax(q @ k.T / sqrt(128), mask=causal) @ v``.
+    KV head h // (nh // nkv), the grouping the [arcee] and [apertus] notes
+    describe (each KV head serves a run of consecutive query heads).
+    [llama]: scores are q.k scaled by 1/sqrt(head_dim), masked causally,
+    softmaxed over keys, and the probabilities weight the values.
 
     Returns (head_out [Sq, nh, hd], scores [nh, Sq, Sk] masked with -inf,
     probs [nh, Sq, Sk]).
@@ -157,7 +160,7 @@ def attention(q, k, v, q_pos, k_pos, key_mask, window):
 
 
 def silu(z):
-    """silu(z) = z / (1 + e^-z)  ([llama] ``g = silu(h @ gate_proj.T)``)."""
+    """silu(z) = z / (1 + e^-z), the gate activation of [llama]'s MLP."""
     z = np.asarray(z, F64)
     return z / (1.0 + np.exp(-z))
 
@@ -168,7 +171,7 @@ def sigmoid(z):
 
 
 def relu2(z):
-    """[arcee] ``relu(up_proj(z)) ** 2``: exactly zero below zero."""
+    """Squared ReLU of the [arcee] MLP: max(z, 0)^2, exactly zero below zero."""
     z = np.asarray(z, F64)
     r = np.maximum(z, 0.0)
     return r * r
@@ -180,7 +183,7 @@ def softplus(z):
 
 
 def xielu(z, alpha_p_raw, alpha_n_raw, beta=0.5, eps=-1e-6):
-    """xIELU of the [apertus] notes ("The MLP has no gate ...").
+    """xIELU, the activation of the ungated [apertus] MLP (section 03).
 
     alpha_p = softplus(raw_p), alpha_n = beta + softplus(raw_n);
     z > 0 : alpha_p z^2 + beta z;
@@ -214,25 +217,25 @@ def round_f32(x):
 # --------------------------------------------------------------------------
 
 def swiglu_mlp(m, w_gate, w_up, w_down):
-    """[llama] ``y = (silu(h @ gate.T) * (h @ up.T)) @ down.T``."""
+    """[llama] gated MLP: down( silu(gate(m)) * up(m) )."""
     n = silu(linear(m, w_gate)) * linear(m, w_up)
     return linear(n, w_down), n
 
 
 def relu2_mlp(m, w_up, w_down):
-    """[arcee] ``mlp(z) = down_proj(relu(up_proj(z)) ** 2)``."""
+    """[arcee] ungated MLP: down( relu(up(m))^2 )."""
     n = relu2(linear(m, w_up))
     return linear(n, w_down), n
 
 
 def xielu_mlp(m, w_up, w_down, alpha_p_raw, alpha_n_raw, beta, eps):
-    """[apertus] ``mlp(z) = down_proj(xielu(up_proj(z)))``."""
+    """[apertus] ungated MLP: down( xielu(up(m)) )."""
     n = xielu(linear(m, w_up), alpha_p_raw, alpha_n_raw, beta, eps)
     return linear(n, w_down), n
 
 
 def route(logits, bias, top_k, route_scale, model_dtype):
-    """The sigmoid router of the [afmoe] notes ("The router: ...").
+    """The sigmoid router of the [afmoe] notes (section 03, on the router).
 
     logits: router.gate's output.  The page states the logits are in the
     model's dtype and are cast to float32 before the sigmoid and the bias
@@ -264,8 +267,8 @@ def moe_mlp(m, W, cfg, logits=None):
 
     routed = sum over slots of w_slot * E_{idx_slot}(m) with the SwiGLU
     expert E_e; shared = the shared SwiGLU expert on every token; the
-    mixture returns routed + shared ("routed_output + shared_expert_output
-    is mlp.output").  ``logits`` may be given to force the router's input
+    mixture returns routed + shared (the [afmoe] notes identify that sum
+    with the MLP's output).  ``logits`` may be given to force the router's input
     (a tap of the implementation under test); otherwise the oracle computes
     them.
     """
@@ -327,10 +330,10 @@ def mlp_forward(m, W, cfg, router_logits=None):
 def qkv_heads(a, W, cfg, positions):
     """Project a [n, H] to per-head q [nh, n, hd], k, v [nkv, n, hd].
 
-    Optional per-head q/k RMSNorm before the rotary ([apertus] "Queries and
-    keys are normed per head, before the rotary": one gain vector for every
-    head), then RoPE unless the block is a full (global) afmoe block
-    ([afmoe] "Rotary runs on the sliding-window blocks only").
+    Optional per-head q/k RMSNorm ahead of the rotary ([apertus] section 03:
+    each head's query and key are normalised, one gain vector shared by all
+    heads), then RoPE unless the block is a full (global) afmoe block
+    ([afmoe] section 03: only the sliding-window blocks rotate).
     """
     nh, nkv, hd = cfg["nh"], cfg["nkv"], cfg["hd"]
     n = a.shape[0]
@@ -375,8 +378,8 @@ def attention_sublayer(x, a, key_mask, W, cfg, rows=None):
     premix = head_out.reshape(R, nh * hd)
     gate = cfg["head_gate"]
     if gate:
-        # [afmoe] "multiplies the heads' outputs by the gate's sigmoid
-        # before o_proj"; the gate is projected from the attention's input.
+        # [afmoe] section 03: the heads' outputs are scaled by the sigmoid
+        # of a gate projected from the attention's input, ahead of o_proj.
         gl = sigmoid(linear(a[rows], W["w_head_gate"]))
         if gate == nh:
             premix = (head_out * gl[:, :, None]).reshape(R, nh * hd)
@@ -386,7 +389,8 @@ def attention_sublayer(x, a, key_mask, W, cfg, rows=None):
             raise ValueError("head gate width must be nh or nh*hd")
     o = linear(premix, W["wo"])
     if cfg["sandwich"]:
-        # [afmoe] h = x + post_attention_layernorm(self_attn(...))
+        # [afmoe] sandwich norm: the attention's output is normed before
+        # it joins the residual stream
         attn_out = rms_norm(o, W["w_post_attn_norm"], cfg["eps"])
     else:
         attn_out = o

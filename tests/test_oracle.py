@@ -107,7 +107,8 @@ def test_residual_identity(w):
 
 
 def test_routed_plus_shared_is_mlp_output():
-    """afmoe notes: routed_output + shared_expert_output is mlp.output."""
+    """afmoe notes, section 03: the routed and shared outputs add up to the
+    MLP's output."""
     w = tiny("moe", sandwich=True, head_gate=4, qk_norm=True)
     x, mask, W = inputs(w)
     r = fwd(w, x, mask, W)
@@ -122,7 +123,8 @@ def test_routed_plus_shared_is_mlp_output():
 # ------------------------------------------------------------------ RMSNorm
 
 def test_rmsnorm_scale_invariant_up_to_eps():
-    """afmoe notes: RMSNorm is scale-invariant up to eps."""
+    """afmoe notes, section 03: scaling the norm's input does not change its
+    output, up to eps."""
     rng = np.random.default_rng(0)
     x = rng.standard_normal((5, 64))
     g = rng.standard_normal(64)
@@ -340,7 +342,8 @@ def test_global_block_queries_are_q_norm_output():
 # -------------------------------------------------------------- activations
 
 def test_relu2_exact_zeros():
-    """arcee notes: torch.equal(acts, relu(pre) ** 2) and zero below zero."""
+    """arcee notes, section 03: the activations equal the squared ReLU of the
+    up projection exactly, so every negative pre-activation gives 0."""
     w = tiny("relu2")
     x, mask, W = inputs(w)
     r = fwd(w, x, mask, W)
@@ -351,7 +354,7 @@ def test_relu2_exact_zeros():
 
 
 def test_xielu_printed_values():
-    """apertus notes, 'Negative pre-activations are not switched off': block
+    """apertus notes, section 03 (the xIELU negative branch): block
     8 prints -0.107 at -1, 1.78 at -5, 10.3 at -20 and a minimum of -0.14
     near -0.63.  One effective alpha_n (solved from the value at -20) must
     reproduce all of them through the raw (pre-softplus) parameterisation."""

@@ -217,6 +217,89 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def weight_shapes(cfg: blk_config) -> dict:
+    """Shape of every weight the configuration reads (name -> tuple)."""
+    H, nh, nkv, hd = cfg.hidden, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    s = {"w_in_norm": (H,), "w_mlp_norm": (H,), "wq": (nh * hd, H),
+         "wk": (nkv * hd, H), "wv": (nkv * hd, H), "wo": (H, nh * hd)}
+    if cfg.sandwich_norm:
+        s["w_post_attn_norm"] = (H,)
+        s["w_post_mlp_norm"] = (H,)
+    if cfg.qk_norm:
+        s["w_q_norm"] = (hd,)
+        s["w_k_norm"] = (hd,)
+    if cfg.head_gate_dim:
+        s["w_head_gate"] = (cfg.head_gate_dim, H)
+    I, k = cfg.intermediate, cfg.mlp_kind
+    if k == BLK_MLP_SWIGLU:
+        s["w_gate"] = (I, H)
+    if k in (BLK_MLP_SWIGLU, BLK_MLP_RELU2, BLK_MLP_XIELU):
+        s["w_up"] = (I, H)
+        s["w_down"] = (H, I)
+    if k == BLK_MLP_MOE:
+        E, Ie, Ish = cfg.num_experts, cfg.moe_intermediate, \
+            cfg.moe_intermediate * cfg.num_shared_experts
+        s.update({"w_router": (E, H), "expert_bias": (E,), "w_e_gate": (E, Ie, H),
+                  "w_e_up": (E, Ie, H), "w_e_down": (E, H, Ie)})
+        if Ish:
+            s.update({"w_sh_gate": (Ish, H), "w_sh_up": (Ish, H), "w_sh_down": (H, Ish)})
+    return s
+
+
+def tap_shapes(cfg: blk_config, B: int, S: int) -> dict:
+    """Shape and blk dtype of every tap of a (B, S) call (name -> (shape, dtype))."""
+    H, nh, nkv, hd, md = cfg.hidden, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+    I = cfg.intermediate
+    E, k = cfg.num_experts, cfg.top_k
+    return {
+        "layer_input": ((B, S, H), md), "attention_norm_output": ((B, S, H), md),
+        "attention_scores": ((B, nh, S, S), BLK_F32), "layer_mid": ((B, S, H), BLK_F32),
+        "mlp_input": ((B, S, H), md), "layer_output": ((B, S, H), BLK_F32),
+        "attention_output": ((B, S, H), BLK_F32), "mlp_output": ((B, S, H), BLK_F32),
+        "router_logits": ((B, S, E), md), "expert_indices": ((B, S, k), BLK_I32),
+        "expert_weights": ((B, S, k), BLK_F32),
+        "attention_queries": ((B, nh, S, hd), md), "attention_keys": ((B, nkv, S, hd), md),
+        "attention_values": ((B, nkv, S, hd), md),
+        "attention_probabilities": ((B, nh, S, S), BLK_F32),
+        "attention_head_outputs": ((B, S, nh, hd), md),
+        "attention_premix": ((B, S, nh * hd), md), "mlp_neurons": ((B, S, I), md),
+        "mlp_activation": ((B, S, I), md), "mlp_norm_output": ((B, S, H), md),
+        "expert_outputs": ((B, S, k, H), md), "routed_output": ((B, S, H), BLK_F32),
+        "shared_expert_output": ((B, S, H), BLK_F32),
+    }
+
+
+def _torch_dtype(blk_dt):
+    import torch
+    return {BLK_F32: torch.float32, BLK_BF16: torch.bfloat16, BLK_I32: torch.int32}[blk_dt]
+
+
+def check_tensor(name, t, shape, blk_dt):
+    """A contiguous device tensor of exactly this shape and dtype, else BlockError
+    (the C ABI sees bare pointers and cannot check any of it)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise BlockError(BLK_E_NULL, f"{name} must be a torch tensor")
+    if t.dtype != _torch_dtype(blk_dt):
+        raise BlockError(BLK_E_DTYPE, f"{name} has dtype {t.dtype}, expected "
+                                      f"{_torch_dtype(blk_dt)}")
+    # the same element count in another shape ([B, S, nh, hd] for
+    # [B, S, nh * hd]) addresses the same bytes
+    if tuple(t.shape) != tuple(shape) and t.numel() != _numel(shape):
+        raise BlockError(BLK_E_SHAPE, f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if not t.is_contiguous():
+        raise BlockError(BLK_E_SHAPE, f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise BlockError(BLK_E_NULL, f"{name} must be a device tensor")
+
+
+def _numel(shape):
+    n = 1
+    for d in shape:
+        n *= d
+    return n
+
+
 class Block:
     """One libblock handle plus the device weights it is called with."""
 
@@ -227,6 +310,18 @@ class Block:
         self.cfg = cfg
         self.h = h
         self.keep = dict(weights)   # keep tensors alive
+        need = weight_shapes(cfg)
+        wdt = {n: cfg.dtype for n in need}
+        wdt["expert_bias"] = BLK_F32
+        for n, shp in need.items():
+            if weights.get(n) is None:
+                self.close()
+                raise BlockError(BLK_E_NULL, f"weight {n} is missing")
+            try:
+                check_tensor(f"weight {n}", weights[n], shp, wdt[n])
+            except BlockError:
+                self.close()
+                raise
         w = blk_weights()
         for n in WEIGHT_FIELDS + WEIGHT_FIELDS_2:
             t = weights.get(n)
@@ -244,7 +339,26 @@ class Block:
         dict name -> (tensor, blk dtype).  Enqueues on `stream` (torch
         stream or raw handle; default: torch's current stream)."""
         import torch
+        if x.dim() != 3:
+            raise BlockError(BLK_E_SHAPE, f"x must be [B, S, hidden], got {tuple(x.shape)}")
         B, S = int(x.shape[0]), int(x.shape[1])
+        c = self.cfg
+        if not (1 <= B <= c.max_batch and 1 <= S <= c.max_seq):
+            raise BlockError(BLK_E_SHAPE, f"(B, S) = ({B}, {S}) outside "
+                                          f"[1, {c.max_batch}] x [1, {c.max_seq}]")
+        check_tensor("x", x, (B, S, c.hidden), c.dtype)
+        check_tensor("y", y, (B, S, c.hidden), c.dtype)
+        if mask is not None:
+            check_tensor("attention_mask", mask, (B, S), BLK_I32)
+        if taps:
+            shapes = tap_shapes(c, B, S)
+            for name, (t, dt) in taps.items():
+                if name not in shapes:
+                    raise BlockError(BLK_E_CONFIG, f"unknown tap {name}")
+                shp, want = shapes[name]
+                if dt != want:
+                    raise BlockError(BLK_E_DTYPE, f"tap {name} must be requested as {want}")
+                check_tensor(f"tap {name}", t, shp, want)
         io = blk_io(x=x.data_ptr(), attention_mask=_ptr(mask), batch=B, seq=S,
                     y=y.data_ptr())
         tp = None
