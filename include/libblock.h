@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BLK_ABI_VERSION 5
+#define BLK_ABI_VERSION 6
 
 typedef enum blk_status {
   BLK_OK = 0,
@@ -277,6 +277,29 @@ blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
 blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
                               const blk_weights* const* layers, int32_t n_layers,
                               void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  One
+ * forward pass exactly as blk_forward (same kernels, same taps, same
+ * checks, same errors), but with no handle: the configuration comes with
+ * the call, and the workspace is a static device array of
+ * BLK_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  cfg->max_batch and cfg->max_seq are ignored;
+ * the workspace is laid out for io->batch x io->seq, and a call whose
+ * workspace would not fit is refused with BLK_E_SHAPE (the message gives
+ * the bytes it would need) before anything is enqueued.  The rotary table
+ * is rebuilt on `stream` by each call (angles in double, as blk_create).
+ * The call allocates no device memory, and no host memory unless it fails
+ * (the error text).  The first call on a device looks the array's address
+ * up once (hipGetSymbolAddress).  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that may overlap on one GPU -- two streams, or two
+ * host threads -- race and must be serialised by the caller.
+ */
+#define BLK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+blk_status blk_forward_noalloc(const blk_config* cfg, const blk_io* io, const blk_weights* w,
+                               const blk_taps* taps, void* stream);
 
 /* Free the workspace and the handle (NULL is ignored). */
 void blk_destroy(blk_handle* h);

@@ -57,7 +57,7 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_abi_version_and_status_names():
-    assert L.blk_abi_version() == L.ABI_VERSION == 5
+    assert L.blk_abi_version() == L.ABI_VERSION == 6
     for code, name in enumerate(["BLK_OK", "BLK_E_NULL", "BLK_E_CONFIG", "BLK_E_SHAPE",
                                  "BLK_E_ALIGN", "BLK_E_DTYPE", "BLK_E_OOM", "BLK_E_HIP"]):
         assert L.blk_status_str(code) == name

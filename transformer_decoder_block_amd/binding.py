@@ -1,7 +1,7 @@
 """ctypes binding of libblock (include/libblock.h), argument marshalling only.
 
 The names mirror the C ABI: ``blk_create``, ``blk_forward``,
-``blk_forward_layers``, ``blk_destroy``,
+``blk_forward_layers``, ``blk_forward_noalloc``, ``blk_destroy``,
 ``blk_status_str``, ``blk_last_error``, ``blk_abi_version``,
 ``blk_workspace_bytes``, and the structs ``blk_config``, ``blk_weights``,
 ``blk_tap``, ``blk_taps``, ``blk_io``.  ``Block`` is a small convenience
@@ -71,7 +71,7 @@ TAP_NAMES = ["layer_input", "attention_norm_output", "attention_scores",
              "mlp_neurons", "expert_outputs", "routed_output", "shared_expert_output",
              "mlp_activation", "mlp_norm_output"]
 
-ABI_VERSION = 5  # the BLK_ABI_VERSION these structs mirror
+ABI_VERSION = 6  # the BLK_ABI_VERSION these structs mirror
 
 
 class blk_taps(C.Structure):
@@ -113,6 +113,10 @@ def load():
     lib.blk_forward_layers.argtypes = [H, C.POINTER(blk_io), C.POINTER(C.POINTER(blk_weights)),
                                        C.c_int32, C.c_void_p]
     lib.blk_forward_layers.restype = C.c_int
+    lib.blk_forward_noalloc.argtypes = [C.POINTER(blk_config), C.POINTER(blk_io),
+                                        C.POINTER(blk_weights), C.POINTER(blk_taps),
+                                        C.c_void_p]
+    lib.blk_forward_noalloc.restype = C.c_int
     lib.blk_destroy.argtypes = [H]
     lib.blk_destroy.restype = None
     lib.blk_status_str.argtypes = [C.c_int]
@@ -145,6 +149,13 @@ def blk_forward(h, io: blk_io, w: blk_weights, taps, stream: int):
     return lib.blk_forward(h, C.byref(io), C.byref(w),
                            C.byref(taps) if taps is not None else None,
                            C.c_void_p(stream))
+
+
+def blk_forward_noalloc(cfg: blk_config, io: blk_io, w: blk_weights, taps, stream: int):
+    lib = load()
+    return lib.blk_forward_noalloc(C.byref(cfg), C.byref(io), C.byref(w),
+                                   C.byref(taps) if taps is not None else None,
+                                   C.c_void_p(stream))
 
 
 def blk_forward_layers(h, io: blk_io, layers, stream: int):

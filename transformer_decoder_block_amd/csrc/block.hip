@@ -15,6 +15,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -46,6 +48,7 @@ struct blk_handle {
        *m = nullptr, *neur = nullptr, *logits = nullptr, *stage = nullptr, *nsh = nullptr,
        *layer_out = nullptr;  // blk_forward_layers: outputs of the layers before the last
   float* split = nullptr;  // GEMM tail-split partial tiles
+  size_t split_bytes = 0;
   float *gate = nullptr, *o = nullptr, *mid = nullptr, *mlp_raw = nullptr, *ew = nullptr,
         *rope_cos = nullptr, *rope_sin = nullptr;
   int *eidx = nullptr, *gcnt = nullptr, *goff = nullptr, *row_token = nullptr,
@@ -79,6 +82,63 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // elements, so that every 128-byte K stage of the down projection's A rows
 // is one cache line (the pad columns are never read: K stays the width).
 static size_t neuron_ld(int I) { return ((size_t)I + 63) & ~(size_t)63; }
+
+// Lay the workspace of h->cfg (sized for max_batch * max_seq tokens) out
+// from `base` and return its size in bytes; with base == nullptr only the
+// size is computed.  Every part starts on a 256-byte boundary.  The GEMMs'
+// K-split scratch gets split_bytes.  Allocates nothing.
+static size_t carve(blk_handle* h, char* base, size_t split_bytes) {
+  const blk_config& c = h->cfg;
+  const size_t es = esize(c.dtype);
+  const size_t T = (size_t)c.max_batch * c.max_seq;
+  const size_t H = c.hidden, nh = c.num_heads, nkv = c.num_kv_heads, hd = c.head_dim;
+  const size_t Sp = ((size_t)c.max_seq + 63) & ~(size_t)63;
+  const bool moe = c.mlp_kind == BLK_MLP_MOE;
+  const size_t kk = moe ? c.top_k : 0;
+  size_t off = 0;
+  auto add = [&](void** dst, size_t bytes) {
+    *dst = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+  };
+  add(&h->a, T * H * es);
+  add(&h->q, T * nh * hd * es);
+  add(&h->k, T * nkv * hd * es);
+  add(&h->vt, (size_t)c.max_batch * nkv * hd * Sp * es);
+  if (c.head_gate_dim) add((void**)&h->gate, T * c.head_gate_dim * 4);
+  add(&h->premix, T * nh * hd * es);
+  if (c.sandwich_norm) add((void**)&h->o, T * H * 4);
+  add((void**)&h->mid, T * H * 4);
+  add(&h->m, T * H * es);
+  add(&h->layer_out, T * H * es);
+  if (!moe) {
+    add(&h->neur, T * neuron_ld(c.intermediate) * es);
+    if (c.sandwich_norm) add((void**)&h->mlp_raw, T * H * 4);
+  } else {
+    const size_t E = c.num_experts;
+    add(&h->logits, T * E * es);
+    add((void**)&h->eidx, T * kk * 4);
+    add((void**)&h->ew, T * kk * 4);
+    add((void**)&h->gcnt, E * 4);
+    add((void**)&h->goff, E * 4);
+    add((void**)&h->hist, (size_t)dispatch_hist_ints(T * kk, (int)E) * 4);
+    add((void**)&h->row_token, T * kk * 4);
+    add((void**)&h->pair_row, T * kk * 4);
+    add((void**)&h->row_weight, T * kk * 4);
+    add(&h->neur, T * kk * c.moe_intermediate * es);
+    add(&h->stage, T * kk * H * es);
+    if (c.num_shared_experts > 0) {
+      add(&h->nsh, T * (size_t)c.moe_intermediate * c.num_shared_experts * es);
+      add((void**)&h->mlp_raw, T * H * 4);
+    }
+  }
+  if (c.use_rope) {
+    add((void**)&h->rope_cos, (size_t)c.max_seq * (hd / 2) * 4);
+    add((void**)&h->rope_sin, (size_t)c.max_seq * (hd / 2) * 4);
+  }
+  add((void**)&h->split, split_bytes);
+  h->split_bytes = split_bytes;
+  return off;
+}
 
 static blk_status check_config(const blk_config* c) {
   if (c->dtype != BLK_F32 && c->dtype != BLK_BF16)
@@ -164,56 +224,9 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
   blk_status st = check_config(cfg);
   if (st != BLK_OK) return st;
   const blk_config& c = *cfg;
-  const size_t es = esize(c.dtype);
-  const size_t T = (size_t)c.max_batch * c.max_seq;
-  const size_t H = c.hidden, nh = c.num_heads, nkv = c.num_kv_heads, hd = c.head_dim;
-  const size_t Sp = ((size_t)c.max_seq + 63) & ~(size_t)63;
-  const bool moe = c.mlp_kind == BLK_MLP_MOE;
-  const size_t kk = moe ? c.top_k : 0;
-
-  struct Part { void** dst; size_t bytes; };
   blk_handle* h = new blk_handle();
   h->cfg = c;
-  std::vector<Part> parts;
-  auto add = [&](void** dst, size_t bytes) { parts.push_back({dst, bytes}); };
-  add(&h->a, T * H * es);
-  add(&h->q, T * nh * hd * es);
-  add(&h->k, T * nkv * hd * es);
-  add(&h->vt, (size_t)c.max_batch * nkv * hd * Sp * es);
-  if (c.head_gate_dim) add((void**)&h->gate, T * c.head_gate_dim * 4);
-  add(&h->premix, T * nh * hd * es);
-  if (c.sandwich_norm) add((void**)&h->o, T * H * 4);
-  add((void**)&h->mid, T * H * 4);
-  add(&h->m, T * H * es);
-  add(&h->layer_out, T * H * es);
-  if (!moe) {
-    add(&h->neur, T * neuron_ld(c.intermediate) * es);
-    if (c.sandwich_norm) add((void**)&h->mlp_raw, T * H * 4);
-  } else {
-    const size_t E = c.num_experts;
-    add(&h->logits, T * E * es);
-    add((void**)&h->eidx, T * kk * 4);
-    add((void**)&h->ew, T * kk * 4);
-    add((void**)&h->gcnt, E * 4);
-    add((void**)&h->goff, E * 4);
-    add((void**)&h->hist, (size_t)dispatch_hist_ints(T * kk, (int)E) * 4);
-    add((void**)&h->row_token, T * kk * 4);
-    add((void**)&h->pair_row, T * kk * 4);
-    add((void**)&h->row_weight, T * kk * 4);
-    add(&h->neur, T * kk * c.moe_intermediate * es);
-    add(&h->stage, T * kk * H * es);
-    if (c.num_shared_experts > 0) {
-      add(&h->nsh, T * (size_t)c.moe_intermediate * c.num_shared_experts * es);
-      add((void**)&h->mlp_raw, T * H * 4);
-    }
-  }
-  add((void**)&h->split, SPLIT_WS_BYTES);
-  if (c.use_rope) {
-    add((void**)&h->rope_cos, (size_t)c.max_seq * (hd / 2) * 4);
-    add((void**)&h->rope_sin, (size_t)c.max_seq * (hd / 2) * 4);
-  }
-  size_t total = 0;
-  for (auto& p : parts) total += (p.bytes + 255) & ~(size_t)255;
+  const size_t total = carve(h, nullptr, SPLIT_WS_BYTES);
   hipGetDevice(&h->device);
   if (hipMalloc((void**)&h->ws, total) != hipSuccess) {
     hipGetLastError();
@@ -221,14 +234,10 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
     return fail(BLK_E_OOM, "hipMalloc of " + std::to_string(total) + " workspace bytes failed");
   }
   h->ws_bytes = total;
-  size_t off = 0;
-  for (auto& p : parts) {
-    *p.dst = h->ws + off;
-    off += (p.bytes + 255) & ~(size_t)255;
-  }
+  carve(h, h->ws, SPLIT_WS_BYTES);
   if (c.use_rope) {
     // rotary angles phi[s, i] = s * theta^(-2i/hd), computed in double
-    const size_t half = hd / 2;
+    const size_t hd = c.head_dim, half = hd / 2;
     std::vector<float> cs(c.max_seq * half), sn(c.max_seq * half);
     for (size_t s = 0; s < (size_t)c.max_seq; ++s)
       for (size_t i = 0; i < half; ++i) {
@@ -406,7 +415,7 @@ GemmParams gp0(const blk_handle* h) {
   GemmParams p;
   memset(&p, 0, sizeof(p));
   p.split_ws = h->split;
-  p.split_ws_bytes = SPLIT_WS_BYTES;
+  p.split_ws_bytes = h->split_bytes;
   return p;
 }
 
@@ -414,8 +423,9 @@ uint32_t bytes32(size_t n) { return (uint32_t)n; }
 
 }  // namespace
 
-extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
-                                  const blk_taps* taps, void* stream_) {
+// Every check of a forward call, before anything is enqueued.
+static blk_status check_forward(const blk_handle* h, const blk_io* io, const blk_weights* w,
+                                const blk_taps* taps) {
   if (!h || !io || !w) return fail(BLK_E_NULL, "handle, io and weights must not be NULL");
   const blk_config& c = h->cfg;
   if (!io->x || !io->y) return fail(BLK_E_NULL, "io.x and io.y must not be NULL");
@@ -426,9 +436,13 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
     return fail(BLK_E_SHAPE, "batch/seq must be in [1, max_batch] x [1, max_seq]");
   blk_status st = check_weights(h, w);
   if (st != BLK_OK) return st;
-  st = check_taps(h, taps);
-  if (st != BLK_OK) return st;
+  return check_taps(h, taps);
+}
 
+// The kernel sequence of one forward (the call has been checked).
+static blk_status enqueue_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
+                                  const blk_taps* taps, void* stream_) {
+  const blk_config& c = h->cfg;
   hipStream_t s = (hipStream_t)stream_;
   const DType dt = c.dtype == BLK_BF16 ? DType::BF16 : DType::F32;
   const int es = (int)esize(c.dtype);
@@ -831,6 +845,13 @@ extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_wei
   return BLK_OK;
 }
 
+extern "C" blk_status blk_forward(blk_handle* h, const blk_io* io, const blk_weights* w,
+                                  const blk_taps* taps, void* stream) {
+  const blk_status st = check_forward(h, io, w, taps);
+  if (st != BLK_OK) return st;
+  return enqueue_forward(h, io, w, taps, stream);
+}
+
 extern "C" blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
                                          const blk_weights* const* layers, int32_t n_layers,
                                          void* stream) {
@@ -860,4 +881,102 @@ extern "C" blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
     src = lio.y;
   }
   return BLK_OK;
+}
+
+// ------------------------------------------------- forward without allocation
+
+// The workspace of blk_forward_noalloc: one copy of this array on every GPU
+// the library runs on, held until the process ends.  In host code its name
+// is only a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, once per device (scratch_base), and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) char scratch[BLK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+void* g_scratch[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`, looked up on
+// the first call on that device with that device current.
+blk_status scratch_base(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    return fail(BLK_E_HIP, "no current HIP device (or more than 64 devices)");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(BLK_E_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                 hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = (char*)g_scratch[dev];
+  return BLK_OK;
+}
+
+// Rotary table of S positions, the same angles as blk_create's host table:
+// phi[s, i] = s * theta^(-2i/hd) in double, cos and sin rounded to float.
+__global__ void __launch_bounds__(256) rope_table_kernel(float* cs, float* sn, int S, int hd,
+                                                         double theta) {
+  const int half = hd / 2;
+  const int64_t n = (int64_t)S * half;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * 256) {
+    const int pos = (int)(e / half), i = (int)(e % half);
+    const double inv_freq = pow(theta, -2.0 * (double)i / (double)hd);
+    const double phi = (double)pos * inv_freq;
+    cs[e] = (float)cos(phi);
+    sn[e] = (float)sin(phi);
+  }
+}
+
+}  // namespace
+
+extern "C" blk_status blk_forward_noalloc(const blk_config* cfg, const blk_io* io,
+                                          const blk_weights* w, const blk_taps* taps,
+                                          void* stream) {
+  if (!cfg || !io || !w) return fail(BLK_E_NULL, "cfg, io and weights must not be NULL");
+  if (io->batch < 1 || io->seq < 1)
+    return fail(BLK_E_SHAPE, "batch and seq must be >= 1");
+  // a handle on the stack, sized for this call's batch and sequence, whose
+  // workspace is the device's scratch array
+  blk_handle h;
+  h.cfg = *cfg;
+  h.cfg.max_batch = io->batch;
+  h.cfg.max_seq = io->seq;
+  blk_status st = check_config(&h.cfg);
+  if (st != BLK_OK) return st;
+  const size_t need = carve(&h, nullptr, 0);
+  if (need > BLK_NOALLOC_SCRATCH_BYTES)
+    return fail(BLK_E_SHAPE, "this batch and sequence need " + std::to_string(need) +
+                                 " bytes of workspace; blk_forward_noalloc holds " +
+                                 std::to_string((size_t)BLK_NOALLOC_SCRATCH_BYTES) +
+                                 " (use blk_create / blk_forward)");
+  st = check_forward(&h, io, w, taps);
+  if (st != BLK_OK) return st;
+  char* base = nullptr;
+  st = scratch_base(&base);
+  if (st != BLK_OK) return st;
+  // what the workspace leaves of the array serves the GEMMs' K split, up
+  // to the handle path's size
+  const size_t split = std::min(SPLIT_WS_BYTES, (BLK_NOALLOC_SCRATCH_BYTES - need) & ~(size_t)255);
+  carve(&h, base, split);
+  h.ws = base;
+  h.ws_bytes = need + split;
+  hipStream_t s = (hipStream_t)stream;
+  if (h.cfg.use_rope) {
+    const int64_t n = (int64_t)io->seq * (h.cfg.head_dim / 2);
+    const int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, s, h.rope_cos, h.rope_sin,
+                       io->seq, h.cfg.head_dim, (double)h.cfg.rope_theta);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(BLK_E_HIP, std::string("rotary table: ") + hipGetErrorString(e));
+  }
+  st = enqueue_forward(&h, io, w, taps, stream);
+  h.ws = nullptr;  // the scratch array is not the handle's to free
+  return st;
 }
