@@ -61,6 +61,7 @@ def kernel_work(w, mask):
     else:
         k = w.top_k
         f["gemm_router"] = ("flop", 2.0 * T * H * w.E)
+        f["gemm_router_topk"] = ("flop", 2.0 * T * H * w.E)
         f["gemm_expert_up"] = ("flop", 2.0 * T * k * H * 2 * w.I_e)
         f["gemm_expert_down"] = ("flop", 2.0 * T * k * w.I_e * H)
         if w.n_shared:

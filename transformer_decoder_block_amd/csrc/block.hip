@@ -120,7 +120,7 @@ static size_t carve(blk_handle* h, char* base, size_t split_bytes) {
     add((void**)&h->ew, T * kk * 4);
     add((void**)&h->gcnt, E * 4);
     add((void**)&h->goff, E * 4);
-    add((void**)&h->hist, (size_t)dispatch_hist_ints(T * kk, (int)E) * 4);
+    add((void**)&h->hist, (size_t)dispatch_hist_ints(T, (int)E) * 4);
     add((void**)&h->row_token, T * kk * 4);
     add((void**)&h->pair_row, T * kk * 4);
     add((void**)&h->row_weight, T * kk * 4);
@@ -706,8 +706,12 @@ static blk_status enqueue_forward(blk_handle* h, const blk_io* io, const blk_wei
   // afmoe mixture
   const int E = c.num_experts, kk = c.top_k, Ie = c.moe_intermediate;
   const int Ish = Ie * c.num_shared_experts;
+  // router: logits in the model dtype, then sigmoid + bias, top-k and the
+  // weights; when one GEMM tile holds every expert of its tokens that all
+  // runs in the GEMM's epilogue, which also counts the dispatch histogram
+  const int rtpc = router_tile_tokens(dt, E);
   {
-    GemmParams p = gp0(h);  // router.gate: logits in the model dtype
+    GemmParams p = gp0(h);  // router.gate
     p.M = T;
     p.N = E;
     p.K = H;
@@ -722,12 +726,25 @@ static blk_status enqueue_forward(blk_handle* h, const blk_io* io, const blk_wei
     p.out = h->logits;
     p.out_f32 = 0;
     p.ldo = E;
-    prof_mark(h, "gemm_router", s);
-    HIP_TRY(gemm(dt, EPI_STORE, p, T, s), "router gemm");
+    if (rtpc) {
+      p.bias = w->expert_bias;
+      p.top_k = kk;
+      p.route_scale = c.route_scale;
+      p.eidx = h->eidx;
+      p.ew = h->ew;
+      p.hist = h->hist;
+      p.hist_nchunks = (T + rtpc - 1) / rtpc;
+      prof_mark(h, "gemm_router_topk", s);
+      HIP_TRY(gemm(dt, EPI_ROUTER, p, T, s), "router gemm + top-k");
+    } else {
+      prof_mark(h, "gemm_router", s);
+      HIP_TRY(gemm(dt, EPI_STORE, p, T, s), "router gemm");
+      prof_mark(h, "topk", s);
+      HIP_TRY(moe_topk(dt, h->logits, w->expert_bias, T, E, kk, c.route_scale, h->eidx, h->ew,
+                       s),
+              "router top-k");
+    }
   }
-  prof_mark(h, "topk", s);
-  HIP_TRY(moe_topk(dt, h->logits, w->expert_bias, T, E, kk, c.route_scale, h->eidx, h->ew, s),
-          "router top-k");
   if (tp.router_logits.ptr)
     HIP_TRY(hipMemcpyAsync(tp.router_logits.ptr, h->logits, (size_t)T * E * es,
                            hipMemcpyDeviceToDevice, s), "router_logits tap");
@@ -739,7 +756,8 @@ static blk_status enqueue_forward(blk_handle* h, const blk_io* io, const blk_wei
                            hipMemcpyDeviceToDevice, s), "expert_weights tap");
   prof_mark(h, "dispatch", s);
   HIP_TRY(moe_dispatch(h->eidx, h->ew, T, kk, E, h->gcnt, h->goff, h->row_token,
-                       h->pair_row, h->row_weight, h->hist, s),
+                       h->pair_row, h->row_weight, h->hist, rtpc ? rtpc : DISPATCH_TOKENS,
+                       rtpc != 0, s),
           "dispatch");
   {
     GemmParams p = gp0(h);  // routed experts: gate/up + SwiGLU

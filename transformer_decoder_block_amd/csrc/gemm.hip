@@ -680,6 +680,118 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, ACC& acc, int
   }
 }
 
+// Router epilogue (afmoe page, section 03, on the router): the tile holds
+// every expert of BM tokens.  The logits are rounded to the model dtype
+// (stored: the router_logits value) and kept in LDS as floats; then one
+// lane per token takes the sigmoid of each rounded logit in double
+// precision, rounded once to float32 (the correctly rounded float32
+// sigmoid), adds the float32 selection bias, and keeps the K largest
+// biased scores by insertion in expert order (ties: the lower expert
+// first); the slot weights are the chosen unbiased sigmoids over their sum
+// (summed in slot order) times route_scale.  The tile's expert counts go to
+// the dispatch histogram.
+// Four lanes per token (lanes 4t .. 4t+3 of a wave): lane `part` keeps the
+// K best of experts part, part + 4, ... by insertion in expert order, then
+// the four sorted lists are merged slot by slot (larger biased score first,
+// the lower expert on ties).  Lane part 0 writes the token's slots and
+// counts them into the tile histogram hcnt.
+template <int K>
+__device__ __forceinline__ void router_select(const GemmParams& p, const float* srow, int tok,
+                                              bool live, int part, int* hcnt) {
+  float bc[K], bs[K];
+  int be[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) { bc[j] = -INFINITY; bs[j] = 0.f; be[j] = 0x7fffffff; }
+  if (live) {
+    for (int e = part; e < p.N; e += 4) {
+      const double l = (double)srow[e];
+      const float sg = (float)(1.0 / (1.0 + exp(-l)));
+      const float c = sg + p.bias[e];
+      // insert (c, e) after every kept score >= c
+#pragma unroll
+      for (int j = K - 1; j >= 1; --j) {
+        const bool up = c > bc[j - 1];     // the entry above moves down
+        const bool here = !up && c > bc[j];
+        bc[j] = up ? bc[j - 1] : (here ? c : bc[j]);
+        bs[j] = up ? bs[j - 1] : (here ? sg : bs[j]);
+        be[j] = up ? be[j - 1] : (here ? e : be[j]);
+      }
+      if (c > bc[0]) { bc[0] = c; bs[0] = sg; be[0] = e; }
+    }
+  }
+  float sel_s[K];
+  int sel_e[K];
+#pragma unroll
+  for (int slot = 0; slot < K; ++slot) {
+    float v = bc[0], sv = bs[0];
+    int ev = be[0];
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {
+      const float ov = __shfl_xor(v, o, 64), os = __shfl_xor(sv, o, 64);
+      const int oe = __shfl_xor(ev, o, 64);
+      if (ov > v || (ov == v && oe < ev)) { v = ov; sv = os; ev = oe; }
+    }
+    if (be[0] == ev) {  // this lane's head was taken: the next one moves up
+#pragma unroll
+      for (int j = 0; j + 1 < K; ++j) { bc[j] = bc[j + 1]; bs[j] = bs[j + 1]; be[j] = be[j + 1]; }
+      bc[K - 1] = -INFINITY;
+      bs[K - 1] = 0.f;
+      be[K - 1] = 0x7fffffff;
+    }
+    sel_s[slot] = sv;
+    sel_e[slot] = ev;
+  }
+  if (!live || part != 0) return;
+  float wsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    if (j < p.top_k) wsum += sel_s[j];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    if (j < p.top_k) {
+      p.eidx[(int64_t)tok * p.top_k + j] = sel_e[j];
+      p.ew[(int64_t)tok * p.top_k + j] = sel_s[j] / wsum * p.route_scale;
+      atomicAdd(&hcnt[sel_e[j]], 1);
+    }
+}
+
+template <typename T, class TL, class ACC>
+__device__ __forceinline__ void router_epilogue(const GemmParams& p, const ACC& acc, int mt,
+                                                int wm, int wn, int lane, int tid,
+                                                float* sc, int* hcnt) {
+  using L = AccL<T, TL::WM, TL::WN>;
+  constexpr int BM = TL::BM, SP = TL::BN + 1;
+#pragma unroll
+  for (int i = 0; i < L::AM; ++i) {
+    const int r = wm * TL::WM + L::row(lane, i);
+    const int64_t grow = (int64_t)mt * BM + r;
+#pragma unroll
+    for (int j = 0; j < L::AN; ++j)
+#pragma unroll
+      for (int q = 0; q < L::QPB; ++q) {
+        const int c = wn * TL::WN + L::col(lane, j, q);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * q + e];
+          sc[r * SP + c + e] = to_f32(from_f32<T>(v[e]));
+        }
+        if (grow < p.M && c < p.N) epi_quad<T, EPI_STORE>(p, grow * p.ldo, c, v, 1.0f);
+      }
+  }
+  for (int e = tid; e < 256; e += TL::NT) hcnt[e] = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < BM; t0 += TL::NT / 4) {
+    const int tl = t0 + tid / 4;
+    const int tok = mt * BM + tl;
+    const bool live = tok < p.M;  // uniform over the token's four lanes
+    if (p.top_k <= 8) router_select<8>(p, sc + tl * SP, tok, live, tid & 3, hcnt);
+    else router_select<16>(p, sc + tl * SP, tok, live, tid & 3, hcnt);
+  }
+  __syncthreads();
+  for (int e = tid; e < p.N; e += TL::NT) p.hist[(int64_t)e * p.hist_nchunks + mt] = hcnt[e];
+}
+
 // ---------------------------------------------------------------- kernel
 
 template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
@@ -697,7 +809,11 @@ gemm_kernel(const GemmParams p) {
   constexpr int SLICE = (WM * (128 + CHT) > 128 * (WM + CHT)) ? WM * (128 + CHT)
                                                                : 128 * (WM + CHT);
   constexpr int MAIN = NS * (BM + BN) * LD;
-  constexpr int SMEM0 = (EPI == EPI_QKV && TL::NW * SLICE > MAIN) ? TL::NW * SLICE : MAIN;
+  // router epilogue: float scores [BM][BN + 1] and 256 int counts
+  constexpr int RSTAGE = (BM * (BN + 1) + 256) * 4 / (int)sizeof(T);
+  constexpr int SMEM0 = (EPI == EPI_QKV && TL::NW * SLICE > MAIN) ? TL::NW * SLICE
+                        : (EPI == EPI_ROUTER && RSTAGE > MAIN) ? RSTAGE
+                                                               : MAIN;
   // grouped: 257 ints of tile prefix sums after the operand tiles
   constexpr int SMEM = GROUPED ? SMEM0 + 257 * 4 / (int)sizeof(T) + 4 : SMEM0;
   __shared__ __attribute__((aligned(1024))) T smem[SMEM];
@@ -887,7 +1003,7 @@ gemm_kernel(const GemmParams p) {
   }
   __syncthreads();  // LDS is free for the epilogue
 
-  if constexpr (!GROUPED && EPI != EPI_QKV) {
+  if constexpr (!GROUPED && EPI != EPI_QKV && EPI != EPI_ROUTER) {
     if (split_slot >= 0) {
       // raw float32 partial tile [BM][BN] (tile-local), finished by the fixup
       float* ws = p.split_ws + (size_t)split_slot * BM * BN;
@@ -906,7 +1022,12 @@ gemm_kernel(const GemmParams p) {
   }
 
   // ---- epilogue: each lane stores its quads (four consecutive columns)
-  if constexpr (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_ROUTER) {
+    float* sc = reinterpret_cast<float*>(smem);
+    int* hcnt = reinterpret_cast<int*>(sc + BM * (BN + 1));
+    router_epilogue<T, TL>(p, acc, mt, wm, wn, lane, tid, sc, hcnt);
+    return;
+  } else if constexpr (EPI == EPI_QKV) {
     // each wave stages its heads in its own slice of the (now idle) LDS
     const int lrow0 = mt * BM + wm * WM;
     T* slice = smem + wave * SLICE;
@@ -1206,7 +1327,7 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   p.split_parts = 1;
   const int num_m = (p.M + TL::BM - 1) / TL::BM;
   const int tiles = num_m * num_n;
-  if constexpr (EPI != EPI_QKV) {
+  if constexpr (EPI != EPI_QKV && EPI != EPI_ROUTER) {
     const int cus = cu_count();
     const int rem = tiles % cus;
     const int nk = (p.K + TL::BK - 1) / TL::BK;
@@ -1242,7 +1363,7 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   }
   hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>),
                      dim3(tiles + p.split_tiles * (p.split_parts - 1)), dim3(TL::NT), 0, s, p);
-  if constexpr (EPI != EPI_QKV) {
+  if constexpr (EPI != EPI_QKV && EPI != EPI_ROUTER) {
     if (p.split_tiles > 0)
       hipLaunchKernelGGL((split_fixup_kernel<T, EPI, TL::BM, TL::BN, TL::WN>),
                          dim3(p.split_tiles), dim3(256), 0, s, p);
@@ -1255,7 +1376,12 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
 using TileL = Tile<bf16, 256, 256, 2, 4, 128, 2>;
 using TileQ = Tile<bf16, 256, 256, 4, 2, 128, 2>;  // 64x128 wave tiles: whole heads per wave
 using TileS = Tile<bf16, 128, 128, 4, 1, 128, 2>;
-using TileR = Tile<bf16, 64, 64, 2, 2, 128, 2>;    // narrow outputs (the router)
+// narrow outputs (the router): 64 x 64 tiles, 256-byte K rows per stage.
+// The router reads its 67 MB operand once, one 64-row block per
+// workgroup; 256-byte rows (two cache lines of each row per stage) measured
+// 38 against 48 us for 128-byte rows at the afmoe shape, where 4 or 8
+// stages of 128-byte rows gained only 1-2 us.
+using TileR = Tile<bf16, 64, 64, 2, 2, 256, 2>;
 using TileF = Tile<float, 128, 128, 4, 1, 128, 2>;
 
 template <typename T, class TL>
@@ -1285,9 +1411,19 @@ static hipError_t dispatch_epi(EpiKind epi, bool grouped, const GemmParams& p,
   }
 }
 
+int router_tile_tokens(DType dt, int E) {
+  if (dt == DType::F32) return E <= TileF::BN ? TileF::BM : 0;
+  return E <= TileR::BN ? TileR::BM : 0;
+}
+
 hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
                 hipStream_t s) {
   const bool grouped = p.gcnt != nullptr;
+  if (epi == EPI_ROUTER) {
+    if (grouped || router_tile_tokens(dt, p.N) == 0) return hipErrorInvalidValue;
+    if (dt == DType::F32) return launch<float, TileF, EPI_ROUTER, false>(p, max_rows, s);
+    return launch<bf16, TileR, EPI_ROUTER, false>(p, max_rows, s);
+  }
   if (dt == DType::F32) return dispatch_epi<float, TileF>(epi, grouped, p, max_rows, s);
   // Large tiles when they still give the chip at least one full wave of
   // workgroups; the 128x128 tile otherwise.

@@ -21,7 +21,10 @@ enum EpiKind : int {
   EPI_XIELU = 4,     // out = model(xielu(acc))
   EPI_QKV = 5,       // q/k/v head-major scatter, q/k norm, rotary, gate
   EPI_MOE_DOWN = 6,  // out[r] = model(row_weight[r] * acc), rows in expert order
-  EPI_SILU = 7       // out = model(silu(acc)): the gated MLP's activation tap
+  EPI_SILU = 7,      // out = model(silu(acc)): the gated MLP's activation tap
+  EPI_ROUTER = 8     // out = model(acc), the router logits [M, N = experts];
+                     // then, per token, sigmoid + bias, top-k, weights, and
+                     // the tile's expert histogram for the dispatch
 };
 
 struct GemmParams {
@@ -57,6 +60,16 @@ struct GemmParams {
   float xa_p, xa_n, xbeta, xeps;
   // EPI_MOE_DOWN
   const float* row_weight;  // the slot weight of each grouped row
+  // EPI_ROUTER: expert bias [N] (float32), top_k, route_scale; outputs the
+  // chosen experts eidx [M, top_k], their weights ew [M, top_k], and
+  // hist[e * hist_nchunks + tile] = pairs of the tile's tokens routed to e
+  const float* bias;
+  int top_k;
+  float route_scale;
+  int* eidx;
+  float* ew;
+  int* hist;
+  int hist_nchunks;
   // EPI_QKV
   void* q; void* k; void* vt;   // [B,nh,S,hd], [B,nkv,S,hd], [B,nkv,hd,Sp]
                                 // with Sp = S rounded up to 64
@@ -79,6 +92,12 @@ struct GemmParams {
 
 hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
                 hipStream_t stream);
+
+// Tokens per tile of the router GEMM with the fused top-k (EPI_ROUTER) for
+// E experts, or 0 when one tile cannot hold every expert of a token (then
+// the logits are stored and moe_topk / moe_dispatch run separately).  The
+// dispatch histogram is kept per chunk of this many tokens.
+int router_tile_tokens(DType dt, int E);
 
 // --------------------------------------------------------------- norms
 // out[t] = model(g * x[t] / sqrt(mean(x[t]^2) + eps)); x float32 or model.
@@ -141,12 +160,16 @@ hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T,
 // row_weight[r] (its pair's slot weight w[pair]); for each pair p,
 // pair_row[p] (its grouped row).  hist is scratch of
 // dispatch_hist_ints(T*k, E) ints.
+// The (token, slot) pairs are counted per chunk of `tpc` tokens (tpc * k
+// pairs): hist[e * nchunks + c].  With `counted`, hist already holds those
+// counts (the router GEMM's fused epilogue wrote them) and only the scan
+// and the write pass run.
 hipError_t moe_dispatch(const int* idx, const float* w, int T, int k, int E, int* gcnt,
                         int* goff, int* row_token, int* pair_row, float* row_weight,
-                        int* hist, hipStream_t s);
-constexpr int DISPATCH_CHUNK = 256;  // (token, slot) pairs per dispatch chunk
-inline int64_t dispatch_hist_ints(int64_t npairs, int E) {
-  return ((npairs + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK) * E;
+                        int* hist, int tpc, bool counted, hipStream_t s);
+constexpr int DISPATCH_TOKENS = 64;  // tokens per dispatch chunk (at least)
+inline int64_t dispatch_hist_ints(int64_t T, int E) {
+  return ((T + DISPATCH_TOKENS - 1) / DISPATCH_TOKENS) * E;
 }
 
 }  // namespace blk

@@ -4,6 +4,10 @@
 // chooses the experts; the weights are the chosen unbiased sigmoids
 // renormalised to sum to route_scale; no expert groups).
 //
+// The router GEMM's epilogue does the sigmoid, bias and top-k itself when
+// one tile holds every expert (gemm.hip, EPI_ROUTER); topk_kernel below
+// serves the wider expert counts.
+//
 // topk: one wavefront per token; lane j owns experts j, j+64, ...  The
 // sigmoid is evaluated in double precision and rounded once to float32, so
 // it is the correctly rounded float32 sigmoid of the logit; the biased
@@ -12,8 +16,10 @@
 // the slots in descending order.
 //
 // dispatch: the T*k (token, slot) pairs are grouped by expert in token-major
-// order (a stable counting sort), with no atomics: per-chunk histograms, a
-// per-expert scan over the chunks, and a per-chunk write pass.
+// order (a stable counting sort), with no float atomics: per-chunk
+// histograms (a chunk is the pairs of one router tile's tokens; the fused
+// router epilogue counts them), a per-expert scan over the chunks, and a
+// per-chunk write pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -93,17 +99,16 @@ hipError_t moe_topk(DType dt, const void* logits, const float* bias, int T, int 
   return hipGetLastError();
 }
 
-constexpr int DCHUNK = DISPATCH_CHUNK;  // pairs per dispatch chunk
-
 // hist[e * nchunks + c] = number of pairs of chunk c routed to expert e
-// (integer LDS atomics: the count does not depend on their order).
+// (integer LDS atomics: the count does not depend on their order).  Chunk c
+// holds the pairs of tokens [c tpc, (c + 1) tpc).
 __global__ void __launch_bounds__(256) dispatch_count(const int* __restrict__ idx, int npairs,
-                                                      int E, int nchunks,
+                                                      int E, int nchunks, int chunk_pairs,
                                                       int* __restrict__ hist) {
   __shared__ int cnt[256];
   const int c = blockIdx.x, t = threadIdx.x;
-  const int p0 = c * DCHUNK;
-  const int n = min(DCHUNK, npairs - p0);
+  const int p0 = c * chunk_pairs;
+  const int n = min(chunk_pairs, npairs - p0);
   cnt[t] = 0;
   __syncthreads();
   for (int i = t; i < n; i += 256) atomicAdd(&cnt[idx[p0 + i]], 1);
@@ -144,7 +149,7 @@ __global__ void __launch_bounds__(256) dispatch_scan(int* __restrict__ hist, int
 // lower lanes holding the same expert.
 __global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx,
                                                      const float* __restrict__ w, int npairs,
-                                                     int k, int E, int nchunks,
+                                                     int k, int E, int nchunks, int chunk_pairs,
                                                      const int* __restrict__ hist,
                                                      const int* __restrict__ gcnt,
                                                      int* __restrict__ goff,
@@ -153,8 +158,8 @@ __global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx
                                                      float* __restrict__ row_weight) {
   __shared__ int base[256];
   const int c = blockIdx.x, l = threadIdx.x;
-  const int p0 = c * DCHUNK;
-  const int n = min(DCHUNK, npairs - p0);
+  const int p0 = c * chunk_pairs;
+  const int n = min(chunk_pairs, npairs - p0);
   // first row of each expert's group: exclusive scan of the totals (lane l
   // owns experts 4l .. 4l+3), plus this chunk's offset inside the group
   {
@@ -206,14 +211,16 @@ __global__ void __launch_bounds__(64) dispatch_write(const int* __restrict__ idx
 
 hipError_t moe_dispatch(const int* idx, const float* w, int T, int k, int E, int* gcnt,
                         int* goff, int* row_token, int* pair_row, float* row_weight,
-                        int* hist, hipStream_t s) {
+                        int* hist, int tpc, bool counted, hipStream_t s) {
   const int npairs = T * k;
-  const int nchunks = (npairs + DCHUNK - 1) / DCHUNK;
-  hipLaunchKernelGGL(dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, npairs, E, nchunks,
-                     hist);
+  const int nchunks = (T + tpc - 1) / tpc;
+  const int chunk_pairs = tpc * k;
+  if (!counted)
+    hipLaunchKernelGGL(dispatch_count, dim3(nchunks), dim3(256), 0, s, idx, npairs, E, nchunks,
+                       chunk_pairs, hist);
   hipLaunchKernelGGL(dispatch_scan, dim3(E), dim3(256), 0, s, hist, nchunks, gcnt);
   hipLaunchKernelGGL(dispatch_write, dim3(nchunks), dim3(64), 0, s, idx, w, npairs, k, E,
-                     nchunks, hist, gcnt, goff, row_token, pair_row, row_weight);
+                     nchunks, chunk_pairs, hist, gcnt, goff, row_token, pair_row, row_weight);
   return hipGetLastError();
 }
 
