@@ -344,9 +344,24 @@ attn_kernel(const AttnParams p) {
     if (myq >= p.S) continue;
     const float inv_l = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
     const int64_t tok = (int64_t)b * p.S + myq;
-    float gh = 1.0f;
-    if (p.gate && p.G == p.nh) gh = p.gate[tok * p.G + h];
     T* orow = (T*)p.out + tok * ((int64_t)p.nh * HD) + h * HD;
+    // gate factors read before the first store (see the bf16 kernel)
+    const bool per_channel = p.gate && p.G != p.nh;
+    const float gh = (p.gate && !per_channel) ? p.gate[tok * p.G + h] : 1.0f;
+    float gv[DB * 16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 g4 = make_float4(gh, gh, gh, gh);
+        if (per_channel)
+          g4 = *reinterpret_cast<const float4*>(p.gate + tok * p.G + h * HD + db * 32 + i * 8 +
+                                                 hf * 4);
+        gv[(db * 4 + i) * 4 + 0] = g4.x;
+        gv[(db * 4 + i) * 4 + 1] = g4.y;
+        gv[(db * 4 + i) * 4 + 2] = g4.z;
+        gv[(db * 4 + i) * 4 + 3] = g4.w;
+      }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -354,11 +369,7 @@ attn_kernel(const AttnParams p) {
         const int d0 = db * 32 + i * 8 + hf * 4;
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float gv = gh;
-          if (p.gate && p.G != p.nh) gv = p.gate[tok * p.G + h * HD + d0 + j];
-          v[j] = o[qi][db][i * 4 + j] * inv_l * gv;
-        }
+        for (int j = 0; j < 4; ++j) v[j] = o[qi][db][i * 4 + j] * inv_l * gv[(db * 4 + i) * 4 + j];
         if constexpr (sizeof(T) == 2) {
           uint2 w;
           w.x = pack2_bf16(v[0], v[1]);
@@ -623,9 +634,28 @@ attn_bf16_kernel(const AttnParams p) {
   if (myq >= p.S) return;
   const float inv_l = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   const int64_t tok = (int64_t)b * p.S + myq;
-  float gh = 1.0f;
-  if (p.gate && p.G == p.nh) gh = p.gate[tok * p.G + h];
   bf16* orow = (bf16*)p.out + tok * ((int64_t)p.nh * HD) + h * HD;
+  // The gate factor of each value the lane stores (one per head, or one per
+  // channel), all read before the first store: a load between the stores
+  // would make every store wait for the ones before it.
+  float gv[DB * 16];
+  if (p.gate && p.G != p.nh) {
+    const float* gr = p.gate + tok * p.G + h * HD;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 g4 = *reinterpret_cast<const float4*>(gr + db * 32 + i * 8 + hf * 4);
+        gv[(db * 4 + i) * 4 + 0] = g4.x;
+        gv[(db * 4 + i) * 4 + 1] = g4.y;
+        gv[(db * 4 + i) * 4 + 2] = g4.z;
+        gv[(db * 4 + i) * 4 + 3] = g4.w;
+      }
+  } else {
+    const float gh = p.gate ? p.gate[tok * p.G + h] : 1.0f;
+#pragma unroll
+    for (int e = 0; e < DB * 16; ++e) gv[e] = gh;
+  }
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -633,11 +663,7 @@ attn_bf16_kernel(const AttnParams p) {
       const int d0 = db * 32 + i * 8 + hf * 4;
       float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float gv = gh;
-        if (p.gate && p.G != p.nh) gv = p.gate[tok * p.G + h * HD + d0 + j];
-        v[j] = o[db][i * 4 + j] * inv_l * gv;
-      }
+      for (int j = 0; j < 4; ++j) v[j] = o[db][i * 4 + j] * inv_l * gv[(db * 4 + i) * 4 + j];
       uint2 w;
       w.x = pack2_bf16(v[0], v[1]);
       w.y = pack2_bf16(v[2], v[3]);
