@@ -1195,8 +1195,17 @@ gemm_persistent_kernel(const GemmParams p) {
   uint32_t a_off[AL], b_off[BL];
   __amdgpu_buffer_rsrc_t rB[BL];
   setup(mt, nt, rb, rc, grp, a_off, b_off, rB);
+#ifndef GEMM_SNAKE
+#define GEMM_SNAKE 1
+#endif
+  // K runs up on a block's even tiles and down on its odd ones: a block's
+  // consecutive tiles share their A rows (or, grouped, their expert's B
+  // rows), so a new tile starts on the stage the tiles before it just read
+  // (still in L2) instead of a stage every block of the XCD misses at once
+  auto kphys = [&](int kt, int dir) { return (GEMM_SNAKE && dir) ? nk - 1 - kt : kt; };
+  int dir = 0;
   int buf = 0;
-  issue(0, 0, a_off, b_off, rB);
+  issue(kphys(0, dir), 0, a_off, b_off, rB);
   while (true) {
 #pragma unroll
     for (int i = 0; i < AM; ++i)
@@ -1220,11 +1229,12 @@ gemm_persistent_kernel(const GemmParams p) {
       // every wave is done with the buffer the next stage refills
       wait_vmcnt<0>();
       __syncthreads();
-      if (kt + 1 < nk) issue(kt + 1, buf ^ 1, a_off, b_off, rB);
-      else if (more) issue(0, buf ^ 1, a2, b2, rB2);
+      if (kt + 1 < nk) issue(kphys(kt + 1, dir), buf ^ 1, a_off, b_off, rB);
+      else if (more) issue(kphys(0, dir ^ 1), buf ^ 1, a2, b2, rB2);
       compute_tile<T, AM, AN, KB>(acc, As(buf), Bs(buf), wm * WM, wn * WN, lane);
       buf ^= 1;
     }
+    dir ^= 1;
     tile_epilogue<T, TL, EPI>(p, acc, mt, nt, rb, rc, wm, wn, lane);
     if (!more) break;
     item = nitem;
