@@ -464,6 +464,22 @@ __device__ __forceinline__ void qkv_epilogue(ACC& acc, const GemmParams& p, int 
       // is passed through unchanged.
       const bool do_norm = p.qk_norm != 0, do_rope = p.use_rope != 0;
       const T* gw = (const T*)(seg == 0 ? p.q_norm_w : p.k_norm_w);
+      // the norm gains of the lane's columns (the same on every row), read
+      // once per head
+      float glo[HB / 2][QPB][4], ghi[HB / 2][QPB][4];
+#pragma unroll
+      for (int jb = 0; jb < HB / 2; ++jb)
+#pragma unroll
+        for (int q = 0; q < QPB; ++q) {
+          const int d = L::col(lane, jb, q);
+          if (do_norm) {
+            load4(gw + d, glo[jb][q]);
+            load4(gw + d + HD / 2, ghi[jb][q]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) glo[jb][q][e] = ghi[jb][q][e] = 1.f;
+          }
+        }
 #pragma unroll
       for (int i = 0; i < AM; ++i) {
         float inv = 1.0f;
@@ -485,35 +501,41 @@ __device__ __forceinline__ void qkv_epilogue(ACC& acc, const GemmParams& p, int 
         const float* cr = p.rope_cos + (int64_t)pos * (HD / 2);
         const float* sr = p.rope_sin + (int64_t)pos * (HD / 2);
         T* srow = lds + lr * QLD;
+        // the row's rotary factors for all of the lane's columns, loaded
+        // together so their latencies overlap
+        float c[HB / 2][QPB][4], sn[HB / 2][QPB][4];
 #pragma unroll
         for (int jb = 0; jb < HB / 2; ++jb)
 #pragma unroll
           for (int q = 0; q < QPB; ++q) {
             const int d = L::col(lane, jb, q);  // low member of the pairs
-            float glo[4] = {1.f, 1.f, 1.f, 1.f}, ghi[4] = {1.f, 1.f, 1.f, 1.f};
-            if (do_norm) {
-              load4(gw + d, glo);
-              load4(gw + d + HD / 2, ghi);
-            }
-            float c[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
             if (do_rope) {
-              load4(cr + d, c);
-              load4(sr + d, sn);
+              load4(cr + d, c[jb][q]);
+              load4(sr + d, sn[jb][q]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) { c[jb][q][e] = 1.f; sn[jb][q][e] = 0.f; }
             }
+          }
+#pragma unroll
+        for (int jb = 0; jb < HB / 2; ++jb)
+#pragma unroll
+          for (int q = 0; q < QPB; ++q) {
+            const int d = L::col(lane, jb, q);
             float olo[4], ohi[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float lo = glo[e] * (acc[i][hh * HB + jb][4 * q + e] * inv);
-              const float hi = ghi[e] * (acc[i][hh * HB + jb + HB / 2][4 * q + e] * inv);
-              olo[e] = do_rope ? lo * c[e] - hi * sn[e] : lo;
-              ohi[e] = do_rope ? hi * c[e] + lo * sn[e] : hi;
+              const float lo = glo[jb][q][e] * (acc[i][hh * HB + jb][4 * q + e] * inv);
+              const float hi = ghi[jb][q][e] * (acc[i][hh * HB + jb + HB / 2][4 * q + e] * inv);
+              olo[e] = do_rope ? lo * c[jb][q][e] - hi * sn[jb][q][e] : lo;
+              ohi[e] = do_rope ? hi * c[jb][q][e] + lo * sn[jb][q][e] : hi;
             }
             store4(srow + d, olo[0], olo[1], olo[2], olo[3]);
             store4(srow + d + HD / 2, ohi[0], ohi[1], ohi[2], ohi[3]);
-            // keep the table loads of later groups from being hoisted here
-            // (their registers would all be live at once)
-            __builtin_amdgcn_sched_barrier(0);
           }
+        // keep the next row block's table loads from being hoisted here
+        // (their registers would be live together with these)
+        __builtin_amdgcn_sched_barrier(0);
       }
       wave_lds_sync();
       T* base = (T*)(seg == 0 ? p.q : p.k);
