@@ -53,14 +53,20 @@ class Run:
     def x64(self):
         return synth.to_f64(self.xst, self.w.dtype)
 
-    def forward(self, taps=(), x=None, mask="same", on_device=False):
+    def forward(self, taps=(), x=None, mask="same", on_device=False, guard=False):
         """Run once; returns dict of float64 numpy arrays (y and taps), or
-        of the device tensors themselves when on_device."""
+        of the device tensors themselves when on_device.  With guard, y and
+        every tap sit between GUARD canary elements on each side, which must
+        be unchanged after the call (else AssertionError naming the buffer)."""
         w = self.w
         x = self.xd if x is None else x
         B, S = int(x.shape[0]), int(x.shape[1])
         m = self.maskd if isinstance(mask, str) else mask
-        y = torch.empty((B, S, w.H), dtype=self.tdt, device="cuda")
+        guarded = {}
+        if guard:
+            y = guarded_empty((B, S, w.H), self.tdt, "y", guarded)
+        else:
+            y = torch.empty((B, S, w.H), dtype=self.tdt, device="cuda")
         shapes = {
             "layer_input": ((B, S, w.H), self.tdt, self.mdt),
             "attention_norm_output": ((B, S, w.H), self.tdt, self.mdt),
@@ -89,11 +95,16 @@ class Run:
         tapt = {}
         for n in taps:
             shp, tdt, bdt = shapes[n]
-            tapt[n] = (torch.full(shp, float("nan"), dtype=tdt, device="cuda")
-                       if tdt != torch.int32 else
-                       torch.full(shp, -1, dtype=tdt, device="cuda"), bdt)
+            if guard:
+                tapt[n] = (guarded_empty(shp, tdt, n, guarded), bdt)
+            else:
+                tapt[n] = (torch.full(shp, float("nan"), dtype=tdt, device="cuda")
+                           if tdt != torch.int32 else
+                           torch.full(shp, -1, dtype=tdt, device="cuda"), bdt)
         self.block.forward(x, y, m, tapt)
         torch.cuda.synchronize()
+        if guard:
+            check_guards(guarded)
         if on_device:
             out = {n: t for n, (t, _) in tapt.items()}
             out["y_raw"] = y
@@ -102,6 +113,36 @@ class Run:
         for n, (t, _) in tapt.items():
             out[n] = t.cpu().numpy() if t.dtype == torch.int32 else host(t)
         return out
+
+
+# Canary words around output buffers: GUARD elements on each side (a
+# multiple of 16 bytes for every element size, so the buffer itself stays
+# 16-byte aligned), filled with a NaN pattern no kernel computes.
+GUARD = 64
+_CANARY = {torch.float32: (torch.int32, 0x7FA5A5A5), torch.bfloat16: (torch.int16, 0x7FA5),
+           torch.int32: (torch.int32, 0x5A5A5A5A)}
+
+
+def guarded_empty(shape, dtype, name, registry):
+    """A contiguous device tensor of `shape` inside a buffer with GUARD
+    canary elements before and after it; the buffer is kept in registry."""
+    n = 1
+    for d in shape:
+        n *= d
+    idt, word = _CANARY[dtype]
+    buf = torch.full((n + 2 * GUARD,), word, dtype=idt, device="cuda")
+    registry[name] = (buf, n, word)
+    return buf.view(dtype)[GUARD:GUARD + n].view(shape)
+
+
+def check_guards(registry):
+    """Every canary word is still in place."""
+    bad = []
+    for name, (buf, n, word) in registry.items():
+        head, tail = buf[:GUARD], buf[GUARD + n:]
+        if not (bool((head == word).all()) and bool((tail == word).all())):
+            bad.append(name)
+    assert not bad, f"writes past the ends of: {bad}"
 
 
 def rel_err(got, ref):

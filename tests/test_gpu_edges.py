@@ -457,3 +457,30 @@ def test_f32_at_larger_size():
     assert rel_err(out["layer_mid"][0][rows], r["layer_mid"]) <= F32_BAR
     assert rel_err(out["layer_output"][0][rows], r["layer_output"]) <= F32_BAR
     assert rel_err(out["y"][0][rows], r["layer_output"]) <= F32_BAR
+
+
+def test_create_reports_oom_and_recovers():
+    """A workspace larger than the free device memory: blk_create returns
+    BLK_E_OOM with a message and no handle, and the library (and the
+    device) work normally once the memory is back.  The condition is made
+    from the host: all but 2 GiB of the device is held by a plain tensor."""
+    from transformer_decoder_block_amd import binding as L
+    w = synth.WORKLOADS["llama7b_bf16"]
+    cfg = L.make_config(w, max_batch=4, max_seq=16384)  # ~6.5 GB of workspace
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    hog = torch.empty(free - (2 << 30), dtype=torch.uint8, device="cuda")
+    try:
+        st, h = L.blk_create(cfg)
+        assert st == L.BLK_E_OOM, L.blk_status_str(st)
+        assert not h
+        assert "hipMalloc" in L.blk_last_error()
+    finally:
+        del hog
+        torch.cuda.empty_cache()
+    st, h = L.blk_create(cfg)
+    assert st == L.BLK_OK, L.blk_last_error()
+    L.blk_destroy(h)
+    run = Run(synth.SMALL["llama_small"])
+    out = run.forward(["layer_output"])
+    assert np.isfinite(out["y"]).all()

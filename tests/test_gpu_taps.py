@@ -182,3 +182,26 @@ def test_interior_taps_leave_output_unchanged(name):
     plain = run.forward()["y_raw"].clone()
     tapped = run.forward(interior_taps(w))["y_raw"]
     assert torch.equal(plain.view(torch.int16), tapped.view(torch.int16))
+
+
+def all_taps(w):
+    return ["layer_input", "attention_scores", "layer_output"] + interior_taps(w)
+
+
+@pytest.mark.parametrize("w", SMALL_BF16 + SMALL_F32[:2], ids=lambda w: w.name)
+def test_tap_canaries_small(w):
+    """Every tap and y between canary words: no kernel writes past either
+    end of a caller's buffer, and the output is the same as without taps."""
+    run = Run(w)
+    plain = run.forward()["y_raw"].clone()
+    out = run.forward(all_taps(w), guard=True)
+    assert torch.equal(plain.view(torch.uint8), out["y_raw"].view(torch.uint8))
+
+
+@pytest.mark.parametrize("name", ["llama7b_bf16", "afmoe_bf16"])
+def test_tap_canaries_full_size(name):
+    """The same at full size, where the GEMMs take their largest tiles, the
+    K-split tail and the persistent grid."""
+    w = synth.WORKLOADS[name]
+    run = Run(w)
+    run.forward(all_taps(w), guard=True, on_device=True)

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libblock.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["block.hip", "gemm.hip", "attention.hip", "norm.hip", "moe.hip"]
+SOURCES = ["block.hip", "gemm.hip", "attention.hip", "norm.hip", "moe.hip", "validate.cpp"]
 ARCH = "gfx950"
 
 

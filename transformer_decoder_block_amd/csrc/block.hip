@@ -22,21 +22,14 @@
 
 #include "../../include/libblock.h"
 #include "kernels.h"
+#include "validate.h"
 
 using namespace blk;
 
-namespace {
-
-thread_local std::string g_err;
-
-blk_status fail(blk_status s, const std::string& msg) {
-  g_err = msg;
-  return s;
-}
-
-size_t esize(int dtype) { return dtype == BLK_BF16 ? 2 : 4; }
-
-}  // namespace
+using blkv::aligned16;
+using blkv::esize;
+using blkv::fail;
+using blkv::neuron_ld;
 
 struct blk_handle {
   blk_config cfg;
@@ -76,152 +69,63 @@ static void prof_mark(blk_handle* h, const char* name, hipStream_t s) {
   ++h->pmarks;
 }
 
-static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
-
-// Row stride of the dense MLP's neuron buffer: the width rounded up to 64
-// elements, so that every 128-byte K stage of the down projection's A rows
-// is one cache line (the pad columns are never read: K stays the width).
-static size_t neuron_ld(int I) { return ((size_t)I + 63) & ~(size_t)63; }
-
-// Lay the workspace of h->cfg (sized for max_batch * max_seq tokens) out
-// from `base` and return its size in bytes; with base == nullptr only the
-// size is computed.  Every part starts on a 256-byte boundary.  The GEMMs'
-// K-split scratch gets split_bytes.  Allocates nothing.
+// Point the handle's workspace views into `base` (laid out for h->cfg:
+// max_batch * max_seq tokens, every part on a 256-byte boundary, the GEMMs'
+// K-split scratch last with split_bytes) and return the workspace size; with
+// base == nullptr only the size is computed.  Allocates nothing.
 static size_t carve(blk_handle* h, char* base, size_t split_bytes) {
   const blk_config& c = h->cfg;
-  const size_t es = esize(c.dtype);
-  const size_t T = (size_t)c.max_batch * c.max_seq;
-  const size_t H = c.hidden, nh = c.num_heads, nkv = c.num_kv_heads, hd = c.head_dim;
-  const size_t Sp = ((size_t)c.max_seq + 63) & ~(size_t)63;
-  const bool moe = c.mlp_kind == BLK_MLP_MOE;
-  const size_t kk = moe ? c.top_k : 0;
-  size_t off = 0;
-  auto add = [&](void** dst, size_t bytes) {
-    *dst = base ? base + off : nullptr;
-    off += (bytes + 255) & ~(size_t)255;
+  const int64_t T = (int64_t)c.max_batch * c.max_seq;
+  const size_t hist = c.mlp_kind == BLK_MLP_MOE ? (size_t)dispatch_hist_ints(T, c.num_experts) : 0;
+  blkv::WsLayout L;
+  blkv::ws_layout(c, hist, split_bytes, &L);
+  auto at = [&](blkv::WsPart part) -> char* {
+    return (base && L.off[part] != blkv::WS_ABSENT) ? base + L.off[part] : nullptr;
   };
-  add(&h->a, T * H * es);
-  add(&h->q, T * nh * hd * es);
-  add(&h->k, T * nkv * hd * es);
-  add(&h->vt, (size_t)c.max_batch * nkv * hd * Sp * es);
-  if (c.head_gate_dim) add((void**)&h->gate, T * c.head_gate_dim * 4);
-  add(&h->premix, T * nh * hd * es);
-  if (c.sandwich_norm) add((void**)&h->o, T * H * 4);
-  add((void**)&h->mid, T * H * 4);
-  add(&h->m, T * H * es);
-  add(&h->layer_out, T * H * es);
-  if (!moe) {
-    add(&h->neur, T * neuron_ld(c.intermediate) * es);
-    if (c.sandwich_norm) add((void**)&h->mlp_raw, T * H * 4);
-  } else {
-    const size_t E = c.num_experts;
-    add(&h->logits, T * E * es);
-    add((void**)&h->eidx, T * kk * 4);
-    add((void**)&h->ew, T * kk * 4);
-    add((void**)&h->gcnt, E * 4);
-    add((void**)&h->goff, E * 4);
-    add((void**)&h->hist, (size_t)dispatch_hist_ints(T, (int)E) * 4);
-    add((void**)&h->row_token, T * kk * 4);
-    add((void**)&h->pair_row, T * kk * 4);
-    add((void**)&h->row_weight, T * kk * 4);
-    add(&h->neur, T * kk * c.moe_intermediate * es);
-    add(&h->stage, T * kk * H * es);
-    if (c.num_shared_experts > 0) {
-      add(&h->nsh, T * (size_t)c.moe_intermediate * c.num_shared_experts * es);
-      add((void**)&h->mlp_raw, T * H * 4);
-    }
-  }
-  if (c.use_rope) {
-    add((void**)&h->rope_cos, (size_t)c.max_seq * (hd / 2) * 4);
-    add((void**)&h->rope_sin, (size_t)c.max_seq * (hd / 2) * 4);
-  }
-  add((void**)&h->split, split_bytes);
+  h->a = at(blkv::WS_A);
+  h->q = at(blkv::WS_Q);
+  h->k = at(blkv::WS_K);
+  h->vt = at(blkv::WS_VT);
+  h->gate = (float*)at(blkv::WS_GATE);
+  h->premix = at(blkv::WS_PREMIX);
+  h->o = (float*)at(blkv::WS_O);
+  h->mid = (float*)at(blkv::WS_MID);
+  h->m = at(blkv::WS_M);
+  h->layer_out = at(blkv::WS_LAYER_OUT);
+  h->neur = at(blkv::WS_NEUR);
+  h->mlp_raw = (float*)at(blkv::WS_MLP_RAW);
+  h->logits = at(blkv::WS_LOGITS);
+  h->eidx = (int*)at(blkv::WS_EIDX);
+  h->ew = (float*)at(blkv::WS_EW);
+  h->gcnt = (int*)at(blkv::WS_GCNT);
+  h->goff = (int*)at(blkv::WS_GOFF);
+  h->hist = (int*)at(blkv::WS_HIST);
+  h->row_token = (int*)at(blkv::WS_ROW_TOKEN);
+  h->pair_row = (int*)at(blkv::WS_PAIR_ROW);
+  h->row_weight = (float*)at(blkv::WS_ROW_WEIGHT);
+  h->stage = at(blkv::WS_STAGE);
+  h->nsh = at(blkv::WS_NSH);
+  h->rope_cos = (float*)at(blkv::WS_ROPE_COS);
+  h->rope_sin = (float*)at(blkv::WS_ROPE_SIN);
+  h->split = (float*)at(blkv::WS_SPLIT);
   h->split_bytes = split_bytes;
-  return off;
-}
-
-static blk_status check_config(const blk_config* c) {
-  if (c->dtype != BLK_F32 && c->dtype != BLK_BF16)
-    return fail(BLK_E_CONFIG, "dtype must be BLK_F32 or BLK_BF16");
-  if (c->hidden <= 0 || c->hidden % 8 || c->hidden > 8192)
-    return fail(BLK_E_CONFIG, "hidden must be a positive multiple of 8, at most 8192");
-  if (c->num_heads <= 0 || c->num_kv_heads <= 0 || c->num_heads % c->num_kv_heads)
-    return fail(BLK_E_CONFIG, "num_heads must be a positive multiple of num_kv_heads");
-  if (c->head_dim != 64 && c->head_dim != 128)
-    return fail(BLK_E_CONFIG, "head_dim must be 64 or 128");
-  if (!(c->rms_eps > 0.f)) return fail(BLK_E_CONFIG, "rms_eps must be > 0");
-  if (c->use_rope && !(c->rope_theta > 0.f))
-    return fail(BLK_E_CONFIG, "rope_theta must be > 0");
-  if (c->sliding_window < 0) return fail(BLK_E_CONFIG, "sliding_window must be >= 0");
-  const int G = c->head_gate_dim;
-  if (G != 0 && G != c->num_heads && G != c->num_heads * c->head_dim)
-    return fail(BLK_E_CONFIG, "head_gate_dim must be 0, num_heads or num_heads*head_dim");
-  if (c->max_batch <= 0 || c->max_seq <= 0)
-    return fail(BLK_E_CONFIG, "max_batch and max_seq must be >= 1");
-  switch (c->mlp_kind) {
-    case BLK_MLP_SWIGLU:
-    case BLK_MLP_RELU2:
-    case BLK_MLP_XIELU:
-      if (c->intermediate <= 0 || c->intermediate % 8)
-        return fail(BLK_E_CONFIG, "intermediate must be a positive multiple of 8");
-      break;
-    case BLK_MLP_MOE:
-      if (c->num_experts <= 0 || c->num_experts > 256)
-        return fail(BLK_E_CONFIG, "num_experts must be in [1, 256]");
-      if (c->top_k <= 0 || c->top_k > 16 || c->top_k > c->num_experts)
-        return fail(BLK_E_CONFIG, "top_k must be in [1, min(16, num_experts)]");
-      if (c->moe_intermediate <= 0 || c->moe_intermediate % 8)
-        return fail(BLK_E_CONFIG, "moe_intermediate must be a positive multiple of 8");
-      if (c->num_shared_experts < 0)
-        return fail(BLK_E_CONFIG, "num_shared_experts must be >= 0");
-      break;
-    default:
-      return fail(BLK_E_CONFIG, "unknown mlp_kind");
-  }
-  // every GEMM operand is addressed with 32-bit byte offsets
-  const double T = (double)c->max_batch * c->max_seq;
-  const double es = (double)esize(c->dtype);
-  double big = T * c->hidden * es;
-  big = fmax(big, T * c->num_heads * c->head_dim * es);
-  if (c->mlp_kind == BLK_MLP_MOE) {
-    big = fmax(big, T * c->top_k * c->moe_intermediate * es);
-    big = fmax(big, T * c->moe_intermediate * c->num_shared_experts * es);
-    big = fmax(big, (double)c->num_experts * c->moe_intermediate * c->hidden * es);
-  } else {
-    big = fmax(big, T * c->intermediate * es);
-    big = fmax(big, (double)c->intermediate * c->hidden * es);
-  }
-  if (big > 4.0e9)
-    return fail(BLK_E_CONFIG, "an operand would exceed 4e9 bytes; lower max_batch*max_seq");
-  return BLK_OK;
+  return L.total;
 }
 
 extern "C" {
 
 int32_t blk_abi_version(void) { return BLK_ABI_VERSION; }
 
-const char* blk_status_str(blk_status s) {
-  switch (s) {
-    case BLK_OK: return "BLK_OK";
-    case BLK_E_NULL: return "BLK_E_NULL";
-    case BLK_E_CONFIG: return "BLK_E_CONFIG";
-    case BLK_E_SHAPE: return "BLK_E_SHAPE";
-    case BLK_E_ALIGN: return "BLK_E_ALIGN";
-    case BLK_E_DTYPE: return "BLK_E_DTYPE";
-    case BLK_E_OOM: return "BLK_E_OOM";
-    case BLK_E_HIP: return "BLK_E_HIP";
-  }
-  return "BLK_E_UNKNOWN";
-}
+const char* blk_status_str(blk_status s) { return blkv::status_str(s); }
 
-const char* blk_last_error(void) { return g_err.c_str(); }
+const char* blk_last_error(void) { return blkv::last_error(); }
 
 size_t blk_workspace_bytes(const blk_handle* h) { return h ? h->ws_bytes : 0; }
 
 blk_status blk_create(const blk_config* cfg, blk_handle** out) {
   if (!cfg || !out) return fail(BLK_E_NULL, "cfg and out must not be NULL");
   *out = nullptr;
-  blk_status st = check_config(cfg);
+  blk_status st = blkv::check_config(cfg);
   if (st != BLK_OK) return st;
   const blk_config& c = *cfg;
   blk_handle* h = new blk_handle();
@@ -236,16 +140,9 @@ blk_status blk_create(const blk_config* cfg, blk_handle** out) {
   h->ws_bytes = total;
   carve(h, h->ws, SPLIT_WS_BYTES);
   if (c.use_rope) {
-    // rotary angles phi[s, i] = s * theta^(-2i/hd), computed in double
-    const size_t hd = c.head_dim, half = hd / 2;
+    const size_t half = c.head_dim / 2;
     std::vector<float> cs(c.max_seq * half), sn(c.max_seq * half);
-    for (size_t s = 0; s < (size_t)c.max_seq; ++s)
-      for (size_t i = 0; i < half; ++i) {
-        const double inv_freq = pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
-        const double phi = (double)s * inv_freq;
-        cs[s * half + i] = (float)cos(phi);
-        sn[s * half + i] = (float)sin(phi);
-      }
+    blkv::rope_table(c, c.max_seq, cs.data(), sn.data());
     if (hipMemcpy(h->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(h->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
       hipFree(h->ws);
@@ -310,100 +207,6 @@ int32_t blk_profile_end(blk_handle* h, int32_t max_entries, const char** names,
 
 namespace {
 
-struct TapCheck {
-  const char* name;
-  const blk_tap* tap;
-  int want;  // required dtype
-  bool allowed;
-};
-
-blk_status check_taps(const blk_handle* h, const blk_taps* t) {
-  if (!t) return BLK_OK;
-  const int md = h->cfg.dtype;
-  const bool moe = h->cfg.mlp_kind == BLK_MLP_MOE;
-  const TapCheck list[] = {
-      {"layer_input", &t->layer_input, md, true},
-      {"attention_norm_output", &t->attention_norm_output, md, true},
-      {"attention_scores", &t->attention_scores, BLK_F32, true},
-      {"layer_mid", &t->layer_mid, BLK_F32, true},
-      {"mlp_input", &t->mlp_input, md, true},
-      {"layer_output", &t->layer_output, BLK_F32, true},
-      {"attention_output", &t->attention_output, BLK_F32, true},
-      {"mlp_output", &t->mlp_output, BLK_F32, true},
-      {"router_logits", &t->router_logits, md, moe},
-      {"expert_indices", &t->expert_indices, BLK_I32, moe},
-      {"expert_weights", &t->expert_weights, BLK_F32, moe},
-      {"attention_queries", &t->attention_queries, md, true},
-      {"attention_keys", &t->attention_keys, md, true},
-      {"attention_values", &t->attention_values, md, true},
-      {"attention_probabilities", &t->attention_probabilities, BLK_F32, true},
-      {"attention_head_outputs", &t->attention_head_outputs, md, true},
-      {"attention_premix", &t->attention_premix, md, true},
-      {"mlp_neurons", &t->mlp_neurons, md, !moe},
-      {"mlp_activation", &t->mlp_activation, md, !moe},
-      {"mlp_norm_output", &t->mlp_norm_output, md, true},
-      {"expert_outputs", &t->expert_outputs, md, moe},
-      {"routed_output", &t->routed_output, BLK_F32, moe},
-      {"shared_expert_output", &t->shared_expert_output, BLK_F32,
-       moe && h->cfg.num_shared_experts > 0},
-  };
-  for (const auto& c : list) {
-    if (!c.tap->ptr) continue;
-    if (!c.allowed)
-      return fail(BLK_E_CONFIG, std::string("tap ") + c.name +
-                                    " does not exist for this block's mlp_kind");
-    if (c.tap->dtype != c.want)
-      return fail(BLK_E_DTYPE, std::string("tap ") + c.name + " must be requested as dtype " +
-                                   std::to_string(c.want));
-    if (!aligned16(c.tap->ptr))
-      return fail(BLK_E_ALIGN, std::string("tap ") + c.name + " is not 16-byte aligned");
-  }
-  return BLK_OK;
-}
-
-struct WNeed {
-  const char* name;
-  const void* p;
-  bool needed;
-};
-
-blk_status check_weights(const blk_handle* h, const blk_weights* w) {
-  const blk_config& c = h->cfg;
-  const int k = c.mlp_kind;
-  const bool moe = k == BLK_MLP_MOE;
-  const WNeed list[] = {
-      {"w_in_norm", w->w_in_norm, true},
-      {"w_post_attn_norm", w->w_post_attn_norm, (bool)c.sandwich_norm},
-      {"w_mlp_norm", w->w_mlp_norm, true},
-      {"w_post_mlp_norm", w->w_post_mlp_norm, (bool)c.sandwich_norm},
-      {"wq", w->wq, true},
-      {"wk", w->wk, true},
-      {"wv", w->wv, true},
-      {"wo", w->wo, true},
-      {"w_q_norm", w->w_q_norm, (bool)c.qk_norm},
-      {"w_k_norm", w->w_k_norm, (bool)c.qk_norm},
-      {"w_head_gate", w->w_head_gate, c.head_gate_dim > 0},
-      {"w_gate", w->w_gate, k == BLK_MLP_SWIGLU},
-      {"w_up", w->w_up, k == BLK_MLP_SWIGLU || k == BLK_MLP_RELU2 || k == BLK_MLP_XIELU},
-      {"w_down", w->w_down, !moe},
-      {"w_router", w->w_router, moe},
-      {"expert_bias", w->expert_bias, moe},
-      {"w_e_gate", w->w_e_gate, moe},
-      {"w_e_up", w->w_e_up, moe},
-      {"w_e_down", w->w_e_down, moe},
-      {"w_sh_gate", w->w_sh_gate, moe && c.num_shared_experts > 0},
-      {"w_sh_up", w->w_sh_up, moe && c.num_shared_experts > 0},
-      {"w_sh_down", w->w_sh_down, moe && c.num_shared_experts > 0},
-  };
-  for (const auto& n : list) {
-    if (!n.needed) continue;
-    if (!n.p) return fail(BLK_E_NULL, std::string("weight ") + n.name + " is NULL");
-    if (!aligned16(n.p))
-      return fail(BLK_E_ALIGN, std::string("weight ") + n.name + " is not 16-byte aligned");
-  }
-  return BLK_OK;
-}
-
 #define HIP_TRY(expr, what)                                                        \
   do {                                                                            \
     hipError_t e_ = (expr);                                                       \
@@ -426,17 +229,8 @@ uint32_t bytes32(size_t n) { return (uint32_t)n; }
 // Every check of a forward call, before anything is enqueued.
 static blk_status check_forward(const blk_handle* h, const blk_io* io, const blk_weights* w,
                                 const blk_taps* taps) {
-  if (!h || !io || !w) return fail(BLK_E_NULL, "handle, io and weights must not be NULL");
-  const blk_config& c = h->cfg;
-  if (!io->x || !io->y) return fail(BLK_E_NULL, "io.x and io.y must not be NULL");
-  if (io->x == io->y) return fail(BLK_E_CONFIG, "io.y must not alias io.x");
-  if (!aligned16(io->x) || !aligned16(io->y))
-    return fail(BLK_E_ALIGN, "io.x and io.y must be 16-byte aligned");
-  if (io->batch < 1 || io->seq < 1 || io->batch > c.max_batch || io->seq > c.max_seq)
-    return fail(BLK_E_SHAPE, "batch/seq must be in [1, max_batch] x [1, max_seq]");
-  blk_status st = check_weights(h, w);
-  if (st != BLK_OK) return st;
-  return check_taps(h, taps);
+  if (!h) return fail(BLK_E_NULL, "handle, io and weights must not be NULL");
+  return blkv::check_forward(h->cfg, io, w, taps);
 }
 
 // The kernel sequence of one forward (the call has been checked).
@@ -875,16 +669,11 @@ extern "C" blk_status blk_forward_layers(blk_handle* h, const blk_io* io,
                                          void* stream) {
   if (!h || !io || !layers) return fail(BLK_E_NULL, "handle, io and layers must not be NULL");
   if (n_layers < 1) return fail(BLK_E_CONFIG, "n_layers must be >= 1");
-  if (!io->x || !io->y) return fail(BLK_E_NULL, "io.x and io.y must not be NULL");
-  if (io->x == io->y) return fail(BLK_E_CONFIG, "io.y must not alias io.x");
-  if (!aligned16(io->x) || !aligned16(io->y))
-    return fail(BLK_E_ALIGN, "io.x and io.y must be 16-byte aligned");
-  const blk_config& c = h->cfg;
-  if (io->batch < 1 || io->seq < 1 || io->batch > c.max_batch || io->seq > c.max_seq)
-    return fail(BLK_E_SHAPE, "batch/seq must be in [1, max_batch] x [1, max_seq]");
+  blk_status st = blkv::check_io(h->cfg, io);
+  if (st != BLK_OK) return st;
   for (int32_t l = 0; l < n_layers; ++l) {
     if (!layers[l]) return fail(BLK_E_NULL, "layer " + std::to_string(l) + " weights are NULL");
-    const blk_status st = check_weights(h, layers[l]);
+    st = blkv::check_weights(h->cfg, layers[l]);
     if (st != BLK_OK) return st;
   }
   // layer l writes y when n_layers - 1 - l is even, else the workspace
@@ -965,7 +754,7 @@ extern "C" blk_status blk_forward_noalloc(const blk_config* cfg, const blk_io* i
   h.cfg = *cfg;
   h.cfg.max_batch = io->batch;
   h.cfg.max_seq = io->seq;
-  blk_status st = check_config(&h.cfg);
+  blk_status st = blkv::check_config(&h.cfg);
   if (st != BLK_OK) return st;
   const size_t need = carve(&h, nullptr, 0);
   if (need > BLK_NOALLOC_SCRATCH_BYTES)
