@@ -256,6 +256,11 @@ def main():
             "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4),
             "traffic": measured_traffic(w.name, dom_name), "kernel": dom_name,
             "flop_per_launch": work[dom_name][1]}
+    if w.dtype == "bf16":
+        # context only (frac is against the published peak): a loop of
+        # register-only bf16 MFMAs on every SIMD of this chip, no memory
+        # traffic, reached 2.1-2.3 PFLOP/s at the clock such a load holds
+        roof["measured_mfma_loop_tflops"] = [2100, 2300]
     tokens = w.T
     value = tokens / (ms_step * 1e-3)
     out = {
