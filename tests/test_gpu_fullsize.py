@@ -8,8 +8,9 @@ sequence, element by element.  The attention and MLP stages are evaluated
 by the oracle at sampled query rows (their causal or window prefix of keys
 is projected in full), chosen to cover the first and last tokens, tile
 edges, the window edge and the padded tail; bars and the stagewise protocol
-are those of test_gpu_parity.py.  (tests/test_gpu_tileq.py checks the
-Q/K/V tile these shapes run on every element, at hidden 256.)  Integer work is
+are those of test_gpu_parity.py.  The per-head queries, keys and values and
+the head outputs are compared on every element of the first and the last
+sequence (test_fullsize_qkv_and_attention_every_element).  Integer work is
 checked on every token: the router's choice over all T tokens equals the
 oracle's choice from the same logits, and y equals the bf16 rounding of
 the float32 layer_output everywhere.
@@ -126,3 +127,84 @@ def test_fullsize_stagewise(name):
         print(f"[fullsize] {name} b={b}: end-to-end rows compared {same.sum()}/{len(rows)}",
               flush=True)
         check_floor(f"{name} b={b}", "end_to_end_y", got, floor)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_qkv_and_attention_every_element(name):
+    """At full size, in the launch configuration bench.py times, on every
+    row of the first and the last sequence:
+
+      * the per-head queries, keys and values (after q/k norm and rotary),
+        every element, against the oracle fed the GPU's own normed stream
+        (each within its one bf16 rounding, as in tests/test_gpu_tileq.py);
+      * every head output against the oracle's attention from the GPU's own
+        q, k, v (so every key and value row the kernel read is checked, at
+        every query);
+      * stage C (head gate, o_proj, residual) from those head outputs, and
+        stage E (the MLP and its residual, the MoE routed by the GPU's own
+        logits) from the GPU's layer_mid and mlp_input, at the stagewise
+        bar."""
+    from tests.test_gpu_tileq import check_rounded as check_rounded_tq
+    w = synth.WORKLOADS[name]
+    print(f"[fullsize-attn] {name}: generating inputs", flush=True)
+    run = Run(w)
+    taps = ["attention_norm_output", "attention_queries", "attention_keys",
+            "attention_values", "attention_head_outputs", "layer_mid", "mlp_input",
+            "layer_output"]
+    if w.mlp == "moe":
+        taps.append("router_logits")
+    d = run.forward(taps, on_device=True)
+    x64 = run.x64()
+    W, cfg = run.W64, w.as_dict()
+    S, g = w.S, w.nh // w.nkv
+    pos = np.arange(S)
+    for b in sorted({0, w.B - 1}):
+        print(f"[fullsize-attn] {name}: sequence {b}", flush=True)
+        mk = None if run.mask is None else run.mask[b]
+        a_tap = host(d["attention_norm_output"][b])
+        q, k, v = ob.qkv_heads(a_tap, W, cfg, pos)
+        q_t = host(d["attention_queries"][b])
+        k_t = host(d["attention_keys"][b])
+        v_t = host(d["attention_values"][b])
+        check_rounded_tq(q_t, q)
+        check_rounded_tq(k_t, k)
+        check_rounded_tq(v_t, v)
+        del q, k, v
+        ho_t = host(d["attention_head_outputs"][b])
+        worst = 0.0
+        for h in range(w.nh):
+            kv = h // g
+            for r0 in range(0, S, 512):
+                rows = np.arange(r0, min(S, r0 + 512))
+                klo = max(0, r0 - w.window + 1) if w.window else 0
+                keys = np.arange(klo, rows[-1] + 1)
+                kmask = None if mk is None else mk[keys]
+                ho, _, probs = ob.attention(q_t[h:h + 1, rows], k_t[kv:kv + 1, keys],
+                                            v_t[kv:kv + 1, keys], rows, keys, kmask,
+                                            w.window)
+                spv = probs[0] @ np.abs(v_t[kv, keys])
+                bound = 2.0 ** -8 * (np.abs(ho[:, 0]) + spv) + 1e-6
+                err = np.abs(ho_t[rows, h] - ho[:, 0]) - bound
+                assert np.all(err <= 0), (b, h, r0, int((err > 0).sum()), float(err.max()))
+                worst = max(worst, float(np.max(np.abs(ho_t[rows, h] - ho[:, 0]) / bound)))
+        # stage C on every row, from the GPU's head outputs
+        premix = ho_t.reshape(S, w.nh * w.hd)
+        if w.head_gate:
+            gl = ob.sigmoid(ob.linear(a_tap, W["w_head_gate"]))
+            premix = (ho_t * gl[:, :, None]).reshape(S, -1) if w.head_gate == w.nh \
+                else premix * gl
+        o = ob.linear(premix, W["wo"])
+        if w.sandwich:
+            o = ob.rms_norm(o, W["w_post_attn_norm"], w.eps)
+        mid_t = host(d["layer_mid"][b])
+        e_c = rel_err(mid_t, x64[b] + o)
+        del premix, o
+        # stage E on every row, from the GPU's layer_mid and mlp_input
+        m_t = host(d["mlp_input"][b])
+        logits = host(d["router_logits"][b]) if w.mlp == "moe" else None
+        mo = ob.mlp_sublayer(mid_t, m_t, W, cfg, router_logits=logits)
+        e_e = rel_err(host(d["layer_output"][b]), mo["layer_output"])
+        print(f"[fullsize-attn] {name} b={b}: q/k/v and every head output within bound "
+              f"(largest |err| / bound {worst:.3f}); every row: stage C {e_c:.4g}, "
+              f"stage E {e_e:.4g}", flush=True)
+        assert e_c <= BF16_BAR and e_e <= BF16_BAR, (e_c, e_e)
