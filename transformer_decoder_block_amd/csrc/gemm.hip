@@ -480,6 +480,15 @@ __device__ __forceinline__ void qkv_epilogue(ACC& acc, const GemmParams& p, int 
             for (int e = 0; e < 4; ++e) glo[jb][q][e] = ghi[jb][q][e] = 1.f;
           }
         }
+      // Rotary factors: when the wave's WM rows are consecutive positions of
+      // one sequence, row block i + 1 sits 16 positions after row block i,
+      // so its factors follow from the angle-addition rule with the factors
+      // of 16 positions (table row 16, the same for every row block): one
+      // table read for the first row block instead of one dependent read
+      // per row block.
+      const int pos0 = row0 % p.S;
+      const bool rec = do_rope && (row0 + WM <= p.M) && (pos0 + WM <= p.S) && (p.S > 16);
+      float c[HB / 2][QPB][4], sn[HB / 2][QPB][4];
 #pragma unroll
       for (int i = 0; i < AM; ++i) {
         float inv = 1.0f;
@@ -501,22 +510,44 @@ __device__ __forceinline__ void qkv_epilogue(ACC& acc, const GemmParams& p, int 
         const float* cr = p.rope_cos + (int64_t)pos * (HD / 2);
         const float* sr = p.rope_sin + (int64_t)pos * (HD / 2);
         T* srow = lds + lr * QLD;
-        // the row's rotary factors for all of the lane's columns, loaded
-        // together so their latencies overlap
-        float c[HB / 2][QPB][4], sn[HB / 2][QPB][4];
+        if (rec && i > 0) {
+          // (c, s) <- (c c16 - s s16, s c16 + c s16)
+          const float* c16 = p.rope_cos + 16 * (HD / 2);
+          const float* s16 = p.rope_sin + 16 * (HD / 2);
 #pragma unroll
-        for (int jb = 0; jb < HB / 2; ++jb)
+          for (int jb = 0; jb < HB / 2; ++jb)
 #pragma unroll
-          for (int q = 0; q < QPB; ++q) {
-            const int d = L::col(lane, jb, q);  // low member of the pairs
-            if (do_rope) {
-              load4(cr + d, c[jb][q]);
-              load4(sr + d, sn[jb][q]);
-            } else {
+            for (int q = 0; q < QPB; ++q) {
+              const int d = L::col(lane, jb, q);
+              float cd[4], sd[4];
+              load4(c16 + d, cd);
+              load4(s16 + d, sd);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) { c[jb][q][e] = 1.f; sn[jb][q][e] = 0.f; }
+              for (int e = 0; e < 4; ++e) {
+                const float cn = c[jb][q][e] * cd[e] - sn[jb][q][e] * sd[e];
+                sn[jb][q][e] = sn[jb][q][e] * cd[e] + c[jb][q][e] * sd[e];
+                c[jb][q][e] = cn;
+              }
+              // one group's step factors live at a time
+              __builtin_amdgcn_sched_barrier(0);
             }
-          }
+        } else {
+          // the row's rotary factors for all of the lane's columns, loaded
+          // together so their latencies overlap
+#pragma unroll
+          for (int jb = 0; jb < HB / 2; ++jb)
+#pragma unroll
+            for (int q = 0; q < QPB; ++q) {
+              const int d = L::col(lane, jb, q);  // low member of the pairs
+              if (do_rope) {
+                load4(cr + d, c[jb][q]);
+                load4(sr + d, sn[jb][q]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { c[jb][q][e] = 1.f; sn[jb][q][e] = 0.f; }
+              }
+            }
+        }
 #pragma unroll
         for (int jb = 0; jb < HB / 2; ++jb)
 #pragma unroll
