@@ -1,12 +1,18 @@
 """Decoder-block prefill throughput of libblock on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--layers N] [--taps none|all]
 
 A step is one forward pass of the whole block (every kernel of the path)
 over one batch of seeded synthetic input already resident in HBM.  The
 default workload is the Llama-7B-shape block (batch 4 x seq 2048, hidden
 4096, 32/32 heads of 128, SwiGLU width 10928, bf16 operands, float32
 accumulation).  Prints one JSON line.
+
+--layers N times a stack of N blocks (each with its own weights) on one
+handle, one blk_forward_layers call per step; --taps all requests every
+tap the block has in each step (the materialising path of the interior
+values).  --workload also takes the NEXT-row shapes of synth.NEXT.
 
 Per-kernel times come from HIP events that libblock records on its own
 stream inside the timed steps (blk_profile_begin/end); the roofline object
@@ -176,6 +182,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="time a stack of this many blocks (each with its own "
+                         "weights) in one blk_forward_layers call per step")
+    ap.add_argument("--taps", choices=["none", "all"], default="none",
+                    help="all: request every tap the block has in each step")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, copy this many MiB device to device "
                          "once (a kernel of known traffic for HBM counter scaling)")
@@ -190,7 +201,10 @@ def main():
     from transformer_decoder_block_amd import binding as L
     from transformer_decoder_block_amd import synth
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.workload(args.workload)
+    if args.layers < 1 or (args.layers > 1 and args.taps != "none"):
+        print(json.dumps({"error": "--layers must be >= 1, and taps are per single block"}))
+        sys.exit(2)
     Wst = synth.make_weights(w)
     xst = synth.make_x(w)
     mask = synth.make_mask(w)
@@ -207,22 +221,55 @@ def main():
     maskd = None if mask is None else torch.from_numpy(mask).cuda()
     y = torch.empty_like(x)
     blk = L.Block(L.make_config(w), Wd)
+    # a stack: layers 2..N get weights of their own (other seeds)
+    extra = [L.Block(L.make_config(w),
+                     {k: dev(v) for k, v in synth.make_weights(
+                         w.replace(seed=w.seed + 1000 * l)).items()})
+             for l in range(1, args.layers)]
+    io = L.blk_io(x=x.data_ptr(), attention_mask=maskd.data_ptr() if maskd is not None else None,
+                  batch=w.B, seq=w.S, y=y.data_ptr())
+    taps = None
+    if args.taps == "all":
+        shapes = L.tap_shapes(blk.cfg, w.B, w.S)
+        names = ["layer_input", "attention_norm_output", "attention_scores", "layer_mid",
+                 "mlp_input", "layer_output", "attention_output", "mlp_output",
+                 "attention_queries", "attention_keys", "attention_values",
+                 "attention_probabilities", "attention_head_outputs", "attention_premix",
+                 "mlp_norm_output"]
+        if w.mlp == "moe":
+            names += ["router_logits", "expert_indices", "expert_weights", "expert_outputs",
+                      "routed_output"] + (["shared_expert_output"] if w.n_shared else [])
+        else:
+            names += ["mlp_neurons", "mlp_activation"]
+        tdt = {L.BLK_F32: torch.float32, L.BLK_BF16: torch.bfloat16, L.BLK_I32: torch.int32}
+        taps = {n: (torch.empty(shapes[n][0], dtype=tdt[shapes[n][1]], device="cuda"),
+                    shapes[n][1]) for n in names}
     stream = torch.cuda.Stream()
+
+    def step():
+        if args.layers > 1:
+            st = L.blk_forward_layers(blk.h, io, [blk.w] + [e.w for e in extra],
+                                      stream.cuda_stream)
+            if st != L.BLK_OK:
+                raise RuntimeError(L.blk_last_error())
+        else:
+            blk.forward(x, y, maskd, taps, stream=stream)
+
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
-            blk.forward(x, y, maskd, stream=stream)
+            step()
     torch.cuda.synchronize()
 
     # timed region: K steps on one stream, per-kernel events recorded inside
     # by the library, plus one event pair per step on the same stream
-    L.blk_profile_begin(blk.h, args.steps)
+    L.blk_profile_begin(blk.h, args.steps * args.layers)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        blk.forward(x, y, maskd, stream=stream)
+        step()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -237,7 +284,7 @@ def main():
         torch.cuda.synchronize()
 
     work = kernel_work(w, mask)
-    flops = total_flops(work)
+    flops = total_flops(work) * args.layers
     per_kernel = {}
     for name, tot_ms, calls in prof:
         avg = tot_ms / max(1, calls)
@@ -266,13 +313,15 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "ms_per_step": round(ms_step, 4), "ms_per_block": round(ms_step / args.layers, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "seq": w.S, "hidden": w.H,
                    "heads": w.nh, "kv_heads": w.nkv, "head_dim": w.hd,
                    "mlp": w.mlp, "intermediate": w.I or w.I_e,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "layers": args.layers,
+                   "taps": args.taps},
         # per-step device time (HIP events on the stream, K steps)
         "step_ms": {"median": round(float(np.median(step_ms)), 4),
                     "p10": round(float(np.quantile(step_ms, 0.1)), 4),
@@ -289,7 +338,7 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.layers == 1 and args.taps == "none":
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
 

@@ -1,5 +1,6 @@
-"""GPU parity at the full sizes of the four bf16 workloads, in the launch
-configuration bench.py times (one handle created for the workload's own
+"""GPU parity at the full sizes of the four bf16 workloads and of the NEXT
+rows' full-size shapes (synth.NEXT), in the launch configuration bench.py
+times (one handle created for the workload's own
 batch and sequence).
 
 Stages A (the attention-input norm) and D (the MLP-input norm, from the
@@ -27,7 +28,9 @@ from tests.test_gpu_parity import BF16_BAR, check_floor, check_scores
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["llama7b_bf16", "arcee_gqa_bf16", "apertus_bf16", "afmoe_bf16"]
+# the four bf16 workloads, then the NEXT rows at full size (the afmoe page's
+# Nano mixture block, its global form, and its dense-first block)
+FULL = ["llama7b_bf16", "arcee_gqa_bf16", "apertus_bf16", "afmoe_bf16"] + list(synth.NEXT)
 
 
 def check_rounded(got, ref):
@@ -53,7 +56,7 @@ def sample_rows(w):
 
 @pytest.mark.parametrize("name", FULL)
 def test_fullsize_stagewise(name):
-    w = synth.WORKLOADS[name]
+    w = synth.workload(name)
     print(f"[fullsize] {name}: generating inputs", flush=True)
     run = Run(w)
     taps = ["attention_norm_output", "layer_mid", "mlp_input", "layer_output"]
@@ -145,7 +148,7 @@ def test_fullsize_qkv_and_attention_every_element(name):
         logits) from the GPU's layer_mid and mlp_input, at the stagewise
         bar."""
     from tests.test_gpu_tileq import check_rounded as check_rounded_tq
-    w = synth.WORKLOADS[name]
+    w = synth.workload(name)
     print(f"[fullsize-attn] {name}: generating inputs", flush=True)
     run = Run(w)
     taps = ["attention_norm_output", "attention_queries", "attention_keys",

@@ -103,6 +103,39 @@ WORKLOADS = {
         E=64, top_k=8, I_e=1024, n_shared=1, route_scale=2.826, seed=5),
 }
 
+# The NEXT rows at full size, on the afmoe page's Nano shapes (hidden 1024,
+# 8 query heads over 2 of 128, a per-channel head gate 1024 -> 1024, q/k
+# norms, sandwich norms), at the token count of the AFMoE workload:
+#   * the mixture block (128 routed experts of width 256, 8 per token, one
+#     shared expert), a sliding-window block with the rotary;
+#   * the same block as a global one (whole causal prefix, no rotary);
+#   * a dense-first block (a dense SwiGLU of width 3072).
+NEXT = {
+    "trinity_nano_moe_bf16": Workload(
+        "trinity_nano_moe_bf16", "bf16", B=2, S=8192, H=1024, nh=8, nkv=2, hd=128,
+        mlp="moe", qk_norm=True, sandwich=True, window=2048, head_gate=1024,
+        E=128, top_k=8, I_e=256, n_shared=1, route_scale=2.826, seed=7),
+    "trinity_nano_global_bf16": Workload(
+        "trinity_nano_global_bf16", "bf16", B=2, S=8192, H=1024, nh=8, nkv=2,
+        hd=128, mlp="moe", qk_norm=True, sandwich=True, window=0, use_rope=False,
+        head_gate=1024, E=128, top_k=8, I_e=256, n_shared=1, route_scale=2.826,
+        seed=8),
+    "trinity_nano_dense_bf16": Workload(
+        "trinity_nano_dense_bf16", "bf16", B=2, S=8192, H=1024, nh=8, nkv=2,
+        hd=128, mlp="swiglu", I=3072, qk_norm=True, sandwich=True, window=2048,
+        head_gate=1024, seed=9),
+}
+
+
+def workload(name: str) -> Workload:
+    """A named workload: the five of the block, or a NEXT-row shape."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in NEXT:
+        return NEXT[name]
+    raise KeyError(f"unknown workload {name}")
+
+
 # Small shapes of every family that the oracle finishes in seconds; each
 # spans several GEMM/attention tiles and ends in a ragged tail.
 SMALL = {
