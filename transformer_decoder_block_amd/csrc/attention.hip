@@ -18,9 +18,9 @@
 // O^T += V^T P^T straight from registers: the keys a lane holds become the
 // K index of that MFMA and the V^T fragment is read in the same key order.
 // exp2 with the 1/sqrt(hd) scale folded into log2(e); the per-key mask
-// (causal edge, window edge, padded keys, keys past the sequence) is two
-// compares per score against per-lane bounds, and the O rescale is
-// skipped when no lane's running max moved.
+// (causal edge, window edge, padded keys, keys past the sequence) is
+// applied only on tiles that need it, and the O rescale is skipped when no
+// lane's running max moved.
 //
 // Workgroups are numbered so that the query heads sharing one KV head and
 // one query block are consecutive and land on the same XCD (shared K/V in
@@ -436,10 +436,11 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// head_dim 64 needs fewer registers and half the LDS: three workgroups per CU
+// head_dim 64 needs fewer registers (at most 128) and half the LDS (32 KiB
+// per workgroup): four workgroups per CU
 template <int HD>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
-                               amdgpu_waves_per_eu(HD == 64 ? 3 : 2, HD == 64 ? 3 : 2)))
+                               amdgpu_waves_per_eu(HD == 64 ? 4 : 2, HD == 64 ? 4 : 2)))
 attn_bf16_kernel(const AttnParams p) {
   using C = BCfg<HD>;
   constexpr int NKS = C::NKS, DB = C::DB;
@@ -574,17 +575,21 @@ attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { x[r] = s0[r]; x[16 + r] = s1[r]; }
     if (!full) {
+      // bit kl of vis: key k0 + kl is visible to the lane's query (causal
+      // bound hi, window bound lo, padding); shifted so that each score's
+      // bit sits at a constant position
       const int hi = myq - k0;
-      const int lo = (p.window > 0) ? myq - p.window + 1 - k0 : -KT;
-      const uint32_t w0 = (uint32_t)(kvalid >> (4 * hf));
-      const uint32_t w1 = (uint32_t)(kvalid >> (32 + 4 * hf));
+      const int lo = (p.window > 0) ? myq - p.window + 1 - k0 : 0;
+      uint64_t vis = kvalid;
+      vis &= hi < 0 ? 0ull : (hi >= 63 ? ~0ull : (2ull << hi) - 1);
+      vis &= lo <= 0 ? ~0ull : (lo > 63 ? 0ull : ~((1ull << lo) - 1));
+      vis >>= 4 * hf;
+      const uint32_t w0 = (uint32_t)vis, w1 = (uint32_t)(vis >> 32);
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const int r = e & 15;
-        const int kl = (e >> 4) * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-        const uint32_t bit = ((e < 16 ? w0 : w1) >> ((r >> 2) * 8 + (r & 3))) & 1u;
-        const bool vis = (kl <= hi) & (kl >= lo) & (bit != 0u);
-        x[e] = vis ? x[e] : -INFINITY;
+        const uint32_t m = 1u << ((r >> 2) * 8 + (r & 3));
+        x[e] = ((e < 16 ? w0 : w1) & m) ? x[e] : -INFINITY;
       }
     }
 

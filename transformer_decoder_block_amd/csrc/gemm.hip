@@ -733,6 +733,148 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, ACC& acc, int
   }
 }
 
+// Epilogue stores through LDS.  In the accumulator layout one store
+// instruction writes sixteen separate pieces of 32 bytes (bf16) or 64 bytes
+// (float32), four lanes per row, and the memory pipeline drains those far
+// more slowly than whole lines: per-tile timestamps put the epilogue at
+// 9-14 us of a 27-103 us tile.  Here each wave writes its 128 x 64
+// sub-tile, already in the output type SE, into an 8 KiB slice of the stage
+// buffer that the tile's last k-stage freed, 8 KiB of rows per pass; then it
+// reads the slice back by rows, so that every global store covers whole
+// row segments of 128 or 256 bytes.  The rows' 16-byte chunks are
+// XOR-swizzled (by (r / 2) mod 8 for 128-byte rows, r mod 16 for 256-byte
+// rows), which keeps the accumulator writes and the row reads free of bank
+// conflicts.  The slice is the wave's own and LDS operations of one wave
+// complete in order, so the passes need no barrier.
+//   pre(i):          called before row block i is written (loads for it)
+//   val(i, j, v):    the four values of quad (i, j) to stage
+//   emit(rr, ch, d): the 16 bytes d of chunk ch of sub-tile row rr
+template <typename SE, int AM, int AN, class PRE, class VAL, class EMIT>
+__device__ __forceinline__ void stage_rows(char* stage, int lane, PRE&& pre, VAL&& val,
+                                           EMIT&& emit) {
+  constexpr int ES = sizeof(SE), RB = 64 * ES, CPR = RB / 16, RP = 8192 / RB;
+  constexpr int PB = RP / 16, RPI = 64 / CPR, NRD = RP / RPI;
+  static_assert(AN == 4 && AM % PB == 0, "64-column wave tiles");
+  auto sw = [](int r) { return ES == 2 ? (r >> 1) & 7 : r & 15; };
+  const int l15 = lane & 15;
+  int woff[AN];
+#pragma unroll
+  for (int j = 0; j < AN; ++j) {
+    const int byte = (16 * j + 4 * (lane >> 4)) * ES;
+    woff[j] = l15 * RB + (((byte >> 4) ^ sw(l15)) << 4) + (byte & 15);
+  }
+  const int rsub = lane / CPR, ch = lane % CPR;
+#pragma unroll
+  for (int h = 0; h < AM / PB; ++h) {
+#pragma unroll
+    for (int ib = 0; ib < PB; ++ib) {
+      const int i = h * PB + ib;
+      pre(i);
+#pragma unroll
+      for (int j = 0; j < AN; ++j) {
+        float v[4];
+        val(i, j, v);
+        char* dst = stage + ib * 16 * RB + woff[j];
+        if constexpr (ES == 2) {
+          uint2 w;
+          w.x = pack2_bf16(v[0], v[1]);
+          w.y = pack2_bf16(v[2], v[3]);
+          *reinterpret_cast<uint2*>(dst) = w;
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NRD; ++k) {
+      const int r = RPI * k + rsub;
+      const uint4 d = *reinterpret_cast<const uint4*>(stage + r * RB + ((ch ^ sw(r)) << 4));
+      emit(16 * PB * h + r, ch, d);
+    }
+  }
+}
+
+// The staged epilogue of a plain (model dtype or float32), MoE-down or
+// residual tile; false when the wave's sub-tile is not one it handles
+// (columns past N, an unaligned row stride, the residual's raw-product tap),
+// which then takes tile_epilogue.
+template <typename T, class TL, int EPI, class ACC>
+__device__ __forceinline__ bool staged_epilogue(const GemmParams& p, const ACC& acc, int mt,
+                                                int nt, int row_begin, int row_count, int wm,
+                                                int wn, int lane_in, char* stage) {
+  static_assert(sizeof(T) == 2 && TL::WN == 64, "bf16, 64-wide wave tiles");
+  using L = AccL<T, TL::WM, TL::WN>;
+  constexpr int AM = L::AM, AN = L::AN;
+  const int col0 = nt * TL::BN + wn * TL::WN;
+  if (col0 + TL::WN > p.N || (p.ldo % 8) != 0) return false;
+  if (EPI == EPI_RESID && p.out_raw) return false;
+  // the lane's offsets are recomputed here rather than kept live across
+  // the tile loop
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int lrow0 = mt * TL::BM + wm * TL::WM;
+  auto none = [](int) {};
+  if constexpr (EPI == EPI_STORE || EPI == EPI_MOE_DOWN) {
+    float wrow[AM];
+#pragma unroll
+    for (int i = 0; i < AM; ++i) {
+      wrow[i] = 1.0f;
+      if constexpr (EPI == EPI_MOE_DOWN) {
+        const int lr = lrow0 + L::row(lane, i);
+        wrow[i] = p.row_weight[row_begin + (lr < row_count ? lr : 0)];
+      }
+    }
+    auto val = [&](int i, int j, float (&v)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = wrow[i] * acc[i][j][e];
+    };
+    if (EPI == EPI_STORE && p.out_f32) {
+      float* out = (float*)p.out + (int64_t)(row_begin + lrow0) * p.ldo + col0;
+      stage_rows<float, AM, AN>(stage, lane, none, val, [&](int rr, int ch, const uint4& d) {
+        if (lrow0 + rr < row_count)
+          *reinterpret_cast<uint4*>(out + (int64_t)rr * p.ldo + ch * 4) = d;
+      });
+    } else {
+      T* out = (T*)p.out + (int64_t)(row_begin + lrow0) * p.ldo + col0;
+      stage_rows<T, AM, AN>(stage, lane, none, val, [&](int rr, int ch, const uint4& d) {
+        if (lrow0 + rr < row_count)
+          *reinterpret_cast<uint4*>(out + (int64_t)rr * p.ldo + ch * 8) = d;
+      });
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    // residual quads in the accumulator layout, row block i + 1 loaded
+    // while block i is staged; the sums are staged as float32
+    float res[2][AN][4];
+    auto load_blk = [&](int i) {
+      const int lr = lrow0 + L::row(lane, i);
+      const int64_t o = (int64_t)(row_begin + (lr < row_count ? lr : 0)) * p.ldo + col0;
+#pragma unroll
+      for (int j = 0; j < AN; ++j) {
+        if (p.resid_f32) load4((const float*)p.resid + o + L::col(lane, j, 0), res[i & 1][j]);
+        else load4((const T*)p.resid + o + L::col(lane, j, 0), res[i & 1][j]);
+      }
+    };
+    load_blk(0);
+    auto pre = [&](int i) {
+      if (i + 1 < AM) load_blk(i + 1);
+    };
+    auto val = [&](int i, int j, float (&v)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = res[i & 1][j][e] + acc[i][j][e];
+    };
+    const int64_t obase = (int64_t)(row_begin + lrow0) * p.ldo + col0;
+    stage_rows<float, AM, AN>(stage, lane, pre, val, [&](int rr, int ch, const uint4& d) {
+      if (lrow0 + rr >= row_count) return;
+      const int64_t o = obase + (int64_t)rr * p.ldo + ch * 4;
+      if (p.out_f32p) *reinterpret_cast<uint4*>(p.out_f32p + o) = d;
+      if (p.out_model)
+        store4((T*)p.out_model + o, __uint_as_float(d.x), __uint_as_float(d.y),
+               __uint_as_float(d.z), __uint_as_float(d.w));
+    });
+  }
+  return true;
+}
+
 // Router epilogue (afmoe page, section 03, on the router): the tile holds
 // every expert of BM tokens.  The logits are rounded to the model dtype
 // (stored: the router_logits value) and kept in LDS as floats; then one
@@ -1108,8 +1250,15 @@ gemm_persistent_kernel(const GemmParams p) {
   static_assert(NS == 2 && EPI != EPI_QKV, "two stages, register epilogue");
   constexpr int RPB = 256 / KB;
   constexpr bool PAIRED = (EPI == EPI_SWIGLU);
+  // epilogue stores staged through LDS (8 waves, each with an 8 KiB slice
+  // of one 64 KiB stage buffer)
+  constexpr bool STAGED = sizeof(T) == 2 && TL::NW == 8 && WN == 64 &&
+                          BM * LD * (int)sizeof(T) == 32768 && BN * LD * (int)sizeof(T) == 32768 &&
+                          (EPI == EPI_STORE || EPI == EPI_MOE_DOWN || EPI == EPI_RESID);
   constexpr int MAIN = NS * (BM + BN) * LD;
-  constexpr int SMEM = GROUPED ? MAIN + 257 * 4 / (int)sizeof(T) + 4 : MAIN;
+  // grouped: the tile prefix (257 ints), then each group's row offset and
+  // row count (256 each), so that looking up a tile reads LDS only
+  constexpr int SMEM = GROUPED ? MAIN + (257 + 512) * 4 / (int)sizeof(T) + 4 : MAIN;
   __shared__ __attribute__((aligned(1024))) T smem[SMEM];
   auto As = [&](int b) { return smem + b * (BM * LD); };
   auto Bs = [&](int b) { return smem + NS * BM * LD + b * (BN * LD); };
@@ -1123,6 +1272,8 @@ gemm_persistent_kernel(const GemmParams p) {
 
   // ---- the tiles: grouped M tiles per expert as in gemm_kernel
   int* tpre = reinterpret_cast<int*>(smem + MAIN);
+  int* sgoff = tpre + 257;
+  int* sgcnt = sgoff + 256;
   int total;
   if constexpr (GROUPED) {
     if (wave == 0) {
@@ -1130,7 +1281,10 @@ gemm_persistent_kernel(const GemmParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int g = 4 * lane + q;
-        c[q] = g < p.ngroups ? (p.gcnt[g] + BM - 1) / BM : 0;
+        const int cnt = g < p.ngroups ? p.gcnt[g] : 0;
+        sgcnt[g] = cnt;
+        sgoff[g] = g < p.ngroups ? p.goff[g] : 0;
+        c[q] = (cnt + BM - 1) / BM;
         sum += c[q];
       }
       int inc = sum;
@@ -1165,8 +1319,8 @@ gemm_persistent_kernel(const GemmParams p) {
       }
       grp = lo;
       mt = t - tpre[lo];
-      rb = p.goff[lo];
-      rc = p.gcnt[lo];
+      rb = sgoff[lo];
+      rc = sgcnt[lo];
     } else {
       tile_coords(id, num_m, num_n, mt, nt);
       rb = 0;
@@ -1183,15 +1337,33 @@ gemm_persistent_kernel(const GemmParams p) {
   const int k_lane = ((lane % CPR) ^ (((wave * RPI + lrowi) / RPB) & (CPR - 1))) * CH;
   const bool a_dense = !GROUPED && p.a_gather == nullptr;
   const uint32_t a_stride = (uint32_t)((int64_t)TL::NW * RPI * p.lda * sizeof(T));
-  auto setup = [&](int mt, int nt, int rb, int rc, int grp, uint32_t (&a_off)[AL],
-                   uint32_t (&b_off)[BL], __amdgpu_buffer_rsrc_t (&rB)[BL]) {
+  // Only a grouped gate/up GEMM gathers its A rows.  The gathered row of
+  // each of the thread's A loads is fetched when the tile is looked up and
+  // consumed when its first stage is issued, a whole tile later.  With
+  // LATE, every other offset of the next tile is computed from its scalars
+  // when its first stage is issued, so nothing per lane stays live across
+  // the k-loop: the grouped and activation kernels spill otherwise (up to
+  // 30 VGPRs, reloaded behind the epilogue's stores).  The others compute
+  // the offsets up front, which measured slightly faster for them.
+  constexpr bool GATHER = GROUPED && PAIRED;
+  constexpr bool LATE = GROUPED || EPI == EPI_RELU2 || EPI == EPI_XIELU || EPI == EPI_SILU;
+  auto src_row = [&](int mt, int rb, int rc, int i) {
+    const int r = mt * BM + (TL::NW * i + wave) * RPI + lrowi;
+    return rb + (r < rc ? r : 0);
+  };
+  auto gather = [&](int mt, int rb, int rc, int (&g)[AL]) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) g[i] = (GATHER && p.a_gather) ? p.a_gather[src_row(mt, rb, rc, i)] : 0;
+  };
+  auto setup = [&](int mt, int nt, int rb, int rc, int grp, const int (&g)[AL],
+                   uint32_t (&a_off)[AL], uint32_t (&b_off)[BL],
+                   __amdgpu_buffer_rsrc_t (&rB)[BL]) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int lrow = (TL::NW * i + wave) * RPI + lrowi;
       const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
       const int r = mt * BM + lrow;
-      int src = rb + (r < rc ? r : 0);
-      if (p.a_gather) src = p.a_gather[src];
+      const int src = (GATHER && p.a_gather) ? g[i] : src_row(mt, rb, rc, i);
       a_off[i] = (r < rc) ? (uint32_t)(((int64_t)src * p.lda + kch * CH) * sizeof(T))
                           : p.a_bytes;
     }
@@ -1245,9 +1417,11 @@ gemm_persistent_kernel(const GemmParams p) {
   if (item >= total) return;
   int mt, nt, rb, rc, grp;
   select(item, mt, nt, rb, rc, grp);
+  int g[AL];
+  gather(mt, rb, rc, g);
   uint32_t a_off[AL], b_off[BL];
   __amdgpu_buffer_rsrc_t rB[BL];
-  setup(mt, nt, rb, rc, grp, a_off, b_off, rB);
+  setup(mt, nt, rb, rc, grp, g, a_off, b_off, rB);
 #ifndef GEMM_SNAKE
 #define GEMM_SNAKE 1
 #endif
@@ -1270,11 +1444,18 @@ gemm_persistent_kernel(const GemmParams p) {
     const int nitem = item + (int)gridDim.x;
     const bool more = nitem < total;
     int mt2 = 0, nt2 = 0, rb2 = 0, rc2 = 0, grp2 = 0;
+    int g2[AL];
     uint32_t a2[AL], b2[BL];
     __amdgpu_buffer_rsrc_t rB2[BL];
     if (more) {
       select(nitem, mt2, nt2, rb2, rc2, grp2);
-      setup(mt2, nt2, rb2, rc2, grp2, a2, b2, rB2);
+      mt2 = __builtin_amdgcn_readfirstlane(mt2);
+      nt2 = __builtin_amdgcn_readfirstlane(nt2);
+      rb2 = __builtin_amdgcn_readfirstlane(rb2);
+      rc2 = __builtin_amdgcn_readfirstlane(rc2);
+      grp2 = __builtin_amdgcn_readfirstlane(grp2);
+      gather(mt2, rb2, rc2, g2);
+      if constexpr (!LATE) setup(mt2, nt2, rb2, rc2, grp2, g2, a2, b2, rB2);
     }
     for (int kt = 0; kt < nk; ++kt) {
       // this thread's loads of stage kt (and the stores of the previous
@@ -1282,13 +1463,27 @@ gemm_persistent_kernel(const GemmParams p) {
       // every wave is done with the buffer the next stage refills
       wait_vmcnt<0>();
       __syncthreads();
-      if (kt + 1 < nk) issue(kphys(kt + 1, dir), buf ^ 1, a_off, b_off, rB);
-      else if (more) issue(kphys(0, dir ^ 1), buf ^ 1, a2, b2, rB2);
+      if (kt + 1 < nk) {
+        issue(kphys(kt + 1, dir), buf ^ 1, a_off, b_off, rB);
+      } else if (more) {
+        if constexpr (LATE) setup(mt2, nt2, rb2, rc2, grp2, g2, a2, b2, rB2);
+        issue(kphys(0, dir ^ 1), buf ^ 1, a2, b2, rB2);
+      }
       compute_tile<T, AM, AN, KB>(acc, As(buf), Bs(buf), wm * WM, wn * WN, lane);
       buf ^= 1;
     }
     dir ^= 1;
-    tile_epilogue<T, TL, EPI>(p, acc, mt, nt, rb, rc, wm, wn, lane);
+    if constexpr (STAGED) {
+      // every wave is done with the last stage's buffer (buf ^ 1): it holds
+      // the staging slices until the next tile's first barrier
+      __syncthreads();
+      char* st = wave < 4 ? (char*)As(buf ^ 1) + wave * 8192
+                          : (char*)Bs(buf ^ 1) + (wave - 4) * 8192;
+      if (!staged_epilogue<T, TL, EPI>(p, acc, mt, nt, rb, rc, wm, wn, lane, st))
+        tile_epilogue<T, TL, EPI>(p, acc, mt, nt, rb, rc, wm, wn, lane);
+    } else {
+      tile_epilogue<T, TL, EPI>(p, acc, mt, nt, rb, rc, wm, wn, lane);
+    }
     if (!more) break;
     item = nitem;
     mt = mt2;
@@ -1296,12 +1491,16 @@ gemm_persistent_kernel(const GemmParams p) {
     rb = rb2;
     rc = rc2;
     grp = grp2;
+    if constexpr (LATE) {
+      setup(mt, nt, rb, rc, grp, g2, a_off, b_off, rB);
+    } else {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) a_off[i] = a2[i];
+      for (int i = 0; i < AL; ++i) a_off[i] = a2[i];
 #pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      b_off[i] = b2[i];
-      rB[i] = rB2[i];
+      for (int i = 0; i < BL; ++i) {
+        b_off[i] = b2[i];
+        rB[i] = rB2[i];
+      }
     }
   }
 }
