@@ -255,6 +255,62 @@ def test_split_tail_tiles():
         assert rel_err(mid[part], att["layer_mid"]) <= BF16_BAR
 
 
+def test_staged_epilogue_ragged_columns():
+    """Hidden 1064 (a multiple of 8, not of 64) at 13312 tokens: o_proj and
+    the down projection are 52 x 5 tiles of 256 x 256 and run persistent.
+    In the last column of tiles, the waves whose 64 columns pass the hidden
+    size take the per-quad epilogue while the others stage their rows
+    through LDS.  layer_mid and layer_output match the oracle on every
+    column of rows in the first, middle and last row tiles, and y is the
+    rounding of the float32 layer_output."""
+    from tests.blockrun import host
+    w = llama("llama_h1064", "bf16", B=1, S=13312, H=1064, nh=8, nkv=2, hd=128, I=512)
+    run = Run(w)
+    d = run.forward(["attention_norm_output", "layer_mid", "mlp_input", "layer_output"],
+                    on_device=True)
+    lo = d["layer_output"].to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(lo, d["y_raw"].view(torch.int16))
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    a_tap = host(d["attention_norm_output"][0])
+    rows = np.array([0, 1, 127, 255, 256, 6655, 6656, 6700, 13055, 13056, 13200, 13311])
+    sel = torch.from_numpy(rows).cuda()
+    mid = host(d["layer_mid"][0][sel])
+    att = ob.attention_sublayer(x64[0], a_tap, None, W, cfg, rows)
+    assert rel_err(mid, att["layer_mid"]) <= BF16_BAR
+    m_t = host(d["mlp_input"][0][sel])
+    mo = ob.mlp_sublayer(mid, m_t, W, cfg)
+    assert rel_err(host(d["layer_output"][0][sel]), mo["layer_output"]) <= BF16_BAR
+
+
+def test_staged_epilogue_ragged_columns_moe():
+    """The AFMoE block at hidden 1064 and 13312 tokens: o_proj and the
+    shared expert's down projection (float32 outputs, 52 x 5 tiles) and the
+    routed experts' down projection (bf16 slot outputs in expert order,
+    grouped) all run persistent with a last column of tiles whose waves
+    partly pass the hidden size.  layer_mid and layer_output match the
+    oracle on every column of the sampled rows, the experts routed from the
+    GPU's own logits."""
+    from tests.blockrun import host
+    w = afmoe("afmoe_h1064", "bf16", B=1, S=13312, E=16, top_k=4, H=1064, nh=8, nkv=2,
+              hd=128, window=2048, head_gate=8, I_e=256)
+    run = Run(w)
+    d = run.forward(["attention_norm_output", "layer_mid", "mlp_input", "layer_output",
+                     "router_logits"], on_device=True)
+    lo = d["layer_output"].to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(lo, d["y_raw"].view(torch.int16))
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    a_tap = host(d["attention_norm_output"][0])
+    rows = np.array([0, 1, 255, 256, 6655, 6656, 13055, 13056, 13311])
+    sel = torch.from_numpy(rows).cuda()
+    mid = host(d["layer_mid"][0][sel])
+    att = ob.attention_sublayer(x64[0], a_tap, None, W, cfg, rows)
+    assert rel_err(mid, att["layer_mid"]) <= BF16_BAR
+    m_t = host(d["mlp_input"][0][sel])
+    logits = host(d["router_logits"][0][sel])
+    mo = ob.mlp_sublayer(mid, m_t, W, cfg, router_logits=logits)
+    assert rel_err(host(d["layer_output"][0][sel]), mo["layer_output"]) <= BF16_BAR
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_trinity_nano_moe_shape(dtype):
     """The afmoe page's Nano shape: 128 routed experts of width 256, top 8,
