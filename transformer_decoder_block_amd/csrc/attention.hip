@@ -385,7 +385,7 @@ attn_kernel(const AttnParams p) {
 // ---------------------------------------------------------------------------
 // bf16 kernel.  One workgroup = 4 waves = 128 queries of one head; wave w
 // owns 32 queries.  Registers are capped so that two workgroups (head_dim
-// 128) or three (head_dim 64) share a CU and one's softmax overlaps the
+// 128) or four (head_dim 64) share a CU and one's softmax overlaps the
 // others' MFMAs.
 //
 // Per 64-key tile a wave computes S^T = K Q^T (lane = query l%32, 32 of the
@@ -523,6 +523,24 @@ attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // Head width 64 leaves the matrix pipe half idle while the lanes run the
+  // softmax, so there the row sums come from one 16x16x32 MFMA per 16-key
+  // step instead of 32 adds per tile: D = Sel P^T, with P^T (16 keys x 32
+  // queries) read as B (32 k x 16 columns; column j holds queries j and
+  // j + 16, each in two 8-key blocks of k).  Row i of Sel selects the
+  // blocks of query j (rows 0, 8) or of query j + 16 (rows 4, 12), the
+  // rows that D places in element 0 of lanes j, j + 16, j + 32, j + 48: so
+  // lacc[0] of every lane is its own query's sum of the probabilities as
+  // rounded for P V^T.  The other rows of Sel are 0.
+  constexpr bool MSUM = HD == 64;
+  bf16x8 sel;
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int i16 = lane & 15, kb = lane >> 4;
+    const bool on = ((i16 == 0 || i16 == 8) && !(kb & 1)) || ((i16 == 4 || i16 == 12) && (kb & 1));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sel[t] = on ? (bf16)1.0f : (bf16)0.0f;
+  }
   const float sl2 = p.scale * 1.4426950408889634f;
 
   issue(kt_lo, 0);
@@ -601,7 +619,8 @@ attn_bf16_kernel(const AttnParams p) {
     if (__ballot(mt > m_run + TAU_L2) != 0ull) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
+      if constexpr (MSUM) lacc[0] *= alpha;
+      else l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -613,9 +632,9 @@ attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       x[e] = fast_exp2(fmaf(x[e], sl2, -msub));
-      psum += x[e];
+      if constexpr (!MSUM) psum += x[e];
     }
-    l_run += psum;
+    if constexpr (!MSUM) l_run += psum;
 
     // ---- O^T += V^T P^T, 16 keys per step
     const char* Vt = Vb(cur);
@@ -631,11 +650,12 @@ attn_bf16_kernel(const AttnParams p) {
             Vt + d * 128 + bslot<128>(d, 2 * j + hf) * 16);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
       }
+      if constexpr (MSUM) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb, lacc, 0, 0, 0);
     }
   }
 
   // ---- normalise, gate, store premix [B*S, nh*hd]
-  const float l_tot = xhalf_sum(l_run);
+  const float l_tot = MSUM ? lacc[0] : xhalf_sum(l_run);
   if (myq >= p.S) return;
   const float inv_l = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   const int64_t tok = (int64_t)b * p.S + myq;
