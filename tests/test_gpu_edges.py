@@ -97,6 +97,9 @@ def check_bf16(run, mask=None):
         logits = None
         if w.mlp == "moe":
             logits = out["router_logits"][b]
+            # the router GEMM itself (its K tail included), from the GPU's
+            # own MLP input; the choice below is then made from its logits
+            assert rel_err(logits, ob.linear(m_tap, W["w_router"])) <= BF16_BAR
             _, idx, wts = ob.route(logits, W["expert_bias"], w.top_k, w.route_scale, "bf16")
             assert np.array_equal(out["expert_indices"][b], idx)
             np.testing.assert_allclose(out["expert_weights"][b], wts, rtol=2e-6, atol=1e-7)
@@ -136,6 +139,15 @@ def test_single_token_moe(dtype):
 def test_ragged_widths(dtype):
     # hidden 264 and MLP width 200: K and N tails in every GEMM and the norms
     CHECK[dtype](Run(llama("llama_ragged", dtype, B=2, S=45, H=264, I=200)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H", [264, 1064])
+def test_ragged_hidden_moe(dtype, H):
+    """The mixture block at hidden sizes that no router stage divides: the
+    router GEMM's last K stage is partial (8 or 40 of its 256 columns), and
+    each of its loads tests its own columns against K."""
+    CHECK[dtype](Run(afmoe(f"afmoe_h{H}", dtype, B=2, S=45, H=H, I_e=200)))
 
 
 def holes_mask(B, S, seed=7):

@@ -97,10 +97,18 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, const vo
 // Address (in elements) of 16-byte chunk c of tile row r, rows of KB bytes.
 // 64 four-byte banks span 256 bytes = 256/KB rows; the slot of chunk c is
 // c xor'ed with the row's index among the rows that share banks.
+// Rows of 256 bytes or more span every bank: the slot is then c xor'ed with
+// the row's low four bits (16 rows, 16 distinct 16-byte slots).
+template <int KB>
+__device__ __forceinline__ int swz_key(int r) {
+  constexpr int CPR = KB / 16, RPB = KB >= 256 ? 1 : 256 / KB;
+  constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
+  return (r / RPB) & MASK;
+}
 template <typename T, int KB>
 __device__ __forceinline__ int swz(int r, int c) {
-  constexpr int CH = 16 / sizeof(T), CPR = KB / 16, RPB = 256 / KB;
-  return r * (CPR * CH) + ((c ^ ((r / RPB) & (CPR - 1))) * CH);
+  constexpr int CH = 16 / sizeof(T), CPR = KB / 16;
+  return r * (CPR * CH) + ((c ^ swz_key<KB>(r)) * CH);
 }
 
 // Accumulator layout of a wave's WM x WN sub-tile: AM x AN blocks, QPB
@@ -997,7 +1005,7 @@ gemm_kernel(const GemmParams p) {
                 CPR = TL::CPR, LD = TL::LD, WM = TL::WM, WN = TL::WN,
                 FM = TL::FM, FN = TL::FN, AL = TL::AL, BL = TL::BL, NS = TL::NS,
                 RPI = TL::RPI, KB = TL::KB;
-  constexpr int RPB = 256 / KB;  // rows that share the 64 banks
+  constexpr int RPB = KB >= 256 ? 1 : 256 / KB;  // rows that share the 64 banks
   constexpr bool PAIRED = (EPI == EPI_SWIGLU);
   constexpr int CHT = 16 / sizeof(T);
   // q/k/v epilogue: each wave stages one head in its own LDS slice
@@ -1101,7 +1109,7 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int lrow = (TL::NW * i + wave) * RPI + lrowi;
-    const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
+    const int kch = (lane % CPR) ^ swz_key<KB>(lrow);
     a_k[i] = kch * CH;
     const int r = mt * BM + lrow;
     int src = row_begin + (r < row_count ? r : 0);
@@ -1120,7 +1128,7 @@ gemm_kernel(const GemmParams p) {
   for (int i = 0; i < BL; ++i) {
     const int lbase = (TL::NW * i + wave) * RPI;
     const int lrow = lbase + lrowi;
-    const int kch = (lane % CPR) ^ ((lrow / RPB) & (CPR - 1));
+    const int kch = (lane % CPR) ^ swz_key<KB>(lrow);
     b_k[i] = kch * CH;
     int seg, n;
     bool ok;
@@ -1143,9 +1151,12 @@ gemm_kernel(const GemmParams p) {
     b_off[i] = ok ? (uint32_t)(((int64_t)n * p.ldb + kch * CH) * sizeof(T))
                   : p.b_bytes[seg];
   }
-  // The k of this lane's chunk is the same in every load instruction (the
-  // swizzle repeats every NW*RPI rows), so one K-tail test covers a stage.
-  static_assert((TL::NW * RPI / RPB) % CPR == 0, "swizzle period divides the load stride");
+  // When the swizzle repeats every NW*RPI rows, the k of this lane's chunk
+  // is the same in every load instruction and one K-tail test covers a
+  // stage; otherwise (rows of 512 bytes) each load tests its own k.
+  constexpr bool K_UNIFORM = (TL::NW * RPI) % 16 == 0 || KB <= 256;
+  static_assert(!K_UNIFORM || KB > 256 || (TL::NW * RPI / RPB) % CPR == 0,
+                "swizzle period divides the load stride");
   const int k_lane = a_k[0];
   // Dense A rows without a gather: offsets are base + i * stride (rows past
   // M read whatever the resource holds or zeros, and are never stored).
@@ -1155,13 +1166,17 @@ gemm_kernel(const GemmParams p) {
     const uint32_t ko = kt * BK * sizeof(T);
     const bool kin = kt * BK + k_lane < p.K;
 #pragma unroll
-    for (int i = 0; i < AL; ++i)
+    for (int i = 0; i < AL; ++i) {
+      const bool ki = K_UNIFORM ? kin : kt * BK + a_k[i] < p.K;
       load16_to_lds(rA, As(buf) + (TL::NW * i + wave) * RPI * LD,
-                    !kin ? p.a_bytes : (a_dense ? a_off[0] + i * a_stride : a_off[i]) + ko);
+                    !ki ? p.a_bytes : (a_dense && K_UNIFORM ? a_off[0] + i * a_stride : a_off[i]) + ko);
+    }
 #pragma unroll
-    for (int i = 0; i < BL; ++i)
+    for (int i = 0; i < BL; ++i) {
+      const bool ki = K_UNIFORM ? kin : kt * BK + b_k[i] < p.K;
       load16_to_lds(rB[i], Bs(buf) + (TL::NW * i + wave) * RPI * LD,
-                    kin ? b_off[i] + ko : 0xffffffffu);
+                    ki ? b_off[i] + ko : 0xffffffffu);
+    }
   };
 
   using L = AccL<T, WM, WN>;
@@ -1638,12 +1653,12 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
 using TileL = Tile<bf16, 256, 256, 2, 4, 128, 2>;
 using TileQ = Tile<bf16, 256, 256, 4, 2, 128, 2>;  // 64x128 wave tiles: whole heads per wave
 using TileS = Tile<bf16, 128, 128, 4, 1, 128, 2>;
-// narrow outputs (the router): 64 x 64 tiles, 256-byte K rows per stage.
+// narrow outputs (the router): 64 x 64 tiles, 512-byte K rows per stage.
 // The router reads its 67 MB operand once, one 64-row block per
-// workgroup; 256-byte rows (two cache lines of each row per stage) measured
-// 38 against 48 us for 128-byte rows at the afmoe shape, where 4 or 8
-// stages of 128-byte rows gained only 1-2 us.
-using TileR = Tile<bf16, 64, 64, 2, 2, 256, 2>;
+// workgroup; longer rows per stage read faster at the afmoe shape (128-byte
+// rows 48 us, 256-byte 37.6, 512-byte 35.0), where 4 or 8 stages of
+// 128-byte rows gained nothing.
+using TileR = Tile<bf16, 64, 64, 2, 2, 512, 2>;
 using TileF = Tile<float, 128, 128, 4, 1, 128, 2>;
 
 template <typename T, class TL>
