@@ -73,3 +73,23 @@ def test_profile_spans(run):
                      "gemm_up", "gemm_down"]
     assert all(p[2] == 2 and p[1] > 0 for p in prof)
     assert L.blk_profile_end(run.block.h) is None
+
+
+def test_two_handles_on_two_streams():
+    """Each handle owns its workspace, so handles on different streams may
+    run at the same time: a dense and a mixture block, and a second handle
+    of the dense configuration with other weights, each enqueued eight times
+    on its own stream without a synchronisation in between, give outputs bit
+    for bit equal to their one-at-a-time forwards."""
+    runs = [Run(synth.SMALL["llama_small"]), Run(synth.SMALL["afmoe_small"]),
+            Run(synth.SMALL["llama_small"].replace(seed=77))]
+    ref = [r.forward()["y_raw"].clone() for r in runs]
+    streams = [torch.cuda.Stream() for _ in runs]
+    ys = [torch.full_like(t, float("nan")) for t in ref]
+    torch.cuda.synchronize()
+    for _ in range(8):
+        for r, s, y in zip(runs, streams, ys):
+            r.block.forward(r.xd, y, r.maskd, None, stream=s)
+    torch.cuda.synchronize()
+    for r, y, y0 in zip(runs, ys, ref):
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), r.w.name
