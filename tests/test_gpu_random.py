@@ -54,3 +54,84 @@ def test_random_config(w):
     print(f"[random] {w}", flush=True)
     run = Run(w)
     CHECK[w.dtype](run, mask=run.mask)
+
+
+# ---------------------------------------------------------------------------
+# The same sweep at the sizes that select the production tiles: 8k-16k
+# tokens with ragged hidden, head and MLP widths, so the persistent 256x256
+# GEMM with every epilogue, the Q/K/V tile, the grouped expert GEMMs, the
+# fused router and the split K tail all run with partial edge tiles.
+# Checked stagewise as the full-size workloads are: stages A and D and the
+# router's logits and choice on every row, the attention and MLP stages at
+# sampled rows (tile edges, window edge, padded tail), y against the bf16
+# rounding of layer_output on every element.
+
+def random_large(i, rng):
+    mlp = ["swiglu", "relu2", "xielu", "moe"][i % 4]
+    hd = int(rng.choice([64, 128]))
+    nkv = int(rng.integers(1, 5))
+    nh = nkv * int(rng.integers(1, 9))
+    while nh * hd > 2048:
+        nh -= nkv
+    B = int(rng.integers(1, 3))
+    S = int(rng.integers(8192 // B, 16384 // B + 1))
+    w = dict(name=f"random_large{i}", dtype="bf16", B=B, S=S,
+             H=8 * int(rng.integers(128, 257)), nh=nh, nkv=nkv, hd=hd, mlp=mlp,
+             qk_norm=bool(rng.random() < 0.5), sandwich=bool(rng.random() < 0.4),
+             window=int(rng.integers(64, S)) if rng.random() < 0.4 else 0,
+             head_gate=[0, nh, nh * hd][int(rng.integers(0, 3))],
+             use_rope=bool(rng.random() < 0.85),
+             pad=int(rng.integers(1, 512)) if (B > 1 and rng.random() < 0.5) else 0,
+             seed=2000 + i)
+    if mlp == "moe":
+        E = int(rng.integers(8, 65))
+        w.update(E=E, top_k=int(rng.integers(1, min(8, E) + 1)),
+                 I_e=8 * int(rng.integers(32, 129)), n_shared=int(rng.integers(0, 2)),
+                 route_scale=float(rng.uniform(1.0, 3.0)))
+    else:
+        w.update(I=8 * int(rng.integers(256, 769)))
+    return synth.Workload(**w)
+
+
+_rng = np.random.default_rng(20261204)
+LARGE = [random_large(i, _rng) for i in range(8)]
+
+
+@pytest.mark.parametrize("w", LARGE, ids=lambda w: w.name)
+def test_random_large_config(w):
+    import torch
+    from oracle import block as ob
+    from tests.blockrun import host, rel_err
+    from tests.test_gpu_fullsize import check_rounded, sample_rows
+    from tests.test_gpu_parity import BF16_BAR
+    print(f"[random-large] {w}", flush=True)
+    run = Run(w)
+    taps = ["attention_norm_output", "layer_mid", "mlp_input", "layer_output"]
+    if w.mlp == "moe":
+        taps += ["router_logits", "expert_indices", "expert_weights"]
+    d = run.forward(taps, on_device=True)
+    assert torch.equal(d["layer_output"].to(torch.bfloat16).view(torch.int16),
+                       d["y_raw"].view(torch.int16))
+    x64, W, cfg = run.x64(), run.W64, w.as_dict()
+    rows = sample_rows(w)
+    for b in sorted({0, w.B - 1}):
+        mk = None if run.mask is None else run.mask[b]
+        a_tap = host(d["attention_norm_output"][b])
+        check_rounded(a_tap, ob.rms_norm(x64[b], W["w_in_norm"], w.eps))
+        mid_all = host(d["layer_mid"][b])
+        m_all = host(d["mlp_input"][b])
+        check_rounded(m_all, ob.mlp_norm(mid_all, W, cfg))
+        logits = None
+        if w.mlp == "moe":
+            lg = host(d["router_logits"][b])
+            assert rel_err(lg, ob.linear(m_all, W["w_router"])) <= BF16_BAR
+            _, idx, wts = ob.route(lg, W["expert_bias"], w.top_k, w.route_scale, "bf16")
+            assert np.array_equal(d["expert_indices"][b].cpu().numpy(), idx)
+            np.testing.assert_allclose(host(d["expert_weights"][b]), wts, rtol=2e-6, atol=1e-7)
+            logits = lg[rows]
+        att = ob.attention_sublayer(x64[b], a_tap, mk, W, cfg, rows)
+        c = rel_err(mid_all[rows], att["layer_mid"])
+        mo = ob.mlp_sublayer(mid_all[rows], m_all[rows], W, cfg, router_logits=logits)
+        e = rel_err(host(d["layer_output"][b, rows]), mo["layer_output"])
+        print(f"[random-large] {w.name} b={b}: C {c:.4g} E {e:.4g}", flush=True)
+        assert c <= BF16_BAR and e <= BF16_BAR, (c, e)
