@@ -1190,6 +1190,13 @@ gemm_kernel(const GemmParams p) {
       for (int r = 0; r < 4 * QPB; ++r) acc[i][j][r] = 0.f;
 
   const int nk_all = (p.K + BK - 1) / BK;
+  // Whole tiles of odd rounds run K downwards.  A round is the 256
+  // workgroups that fill the chip's 256 CUs once (the large tiles hold one
+  // per CU); an XCD's consecutive rounds share their A panels, so a tile of
+  // an odd round starts on the stages the round before ended on, still in
+  // L2.  The sum runs in the other order on those tiles (float32).
+  const bool rev = split_slot < 0 && ((blockIdx.x / 256) & 1);
+  auto kphys = [&](int k) { return rev ? nk_all - 1 - k : k; };
   // K stages [k0, k0 + nk): all of them, or part q of S (S <= nk_all)
   const int sp_q = split_slot >= 0 ? split_slot % p.split_parts : 0;
   const int sp_n = split_slot >= 0 ? p.split_parts : 1;
@@ -1197,7 +1204,7 @@ gemm_kernel(const GemmParams p) {
   const int nk = (sp_q + 1) * nk_all / sp_n - k0;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(k0 + st, st);
+    if (st < nk) issue(kphys(k0 + st), st);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt % NS;
     // this thread's loads of stage kt have landed (the loads of the later
@@ -1208,7 +1215,7 @@ gemm_kernel(const GemmParams p) {
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (kt + NS - 1 < nk) issue(k0 + kt + NS - 1, (kt + NS - 1) % NS);
+    if (kt + NS - 1 < nk) issue(kphys(k0 + kt + NS - 1), (kt + NS - 1) % NS);
     compute_tile<T, AM, AN, KB>(acc, As(cur), Bs(cur), wm * WM, wn * WN, lane);
   }
   __syncthreads();  // LDS is free for the epilogue
