@@ -6,7 +6,8 @@
 // One workgroup of WGM x WGN wavefronts (4: one per SIMD, or 8: two per
 // SIMD) computes a BM x BN tile; each wave owns a (BM/WGM) x (BN/WGN)
 // sub-tile made of 32x32 MFMA blocks.  K is consumed in
-// tiles of 128 bytes per row (64 bf16 / 32 fp32).  Operand tiles go from
+// tiles of 128 bytes per row (64 bf16 / 32 fp32; the router's narrow tile
+// takes 512).  Operand tiles go from
 // global memory straight into LDS (buffer_load ... lds: no VGPR staging),
 // double-buffered: the loads of K-tile k+1 are issued right after the
 // barrier that opens K-tile k and land while its MFMAs run, so one barrier
@@ -14,7 +15,8 @@
 // resource size, which covers ragged M/N edges and the K tail.
 //
 // LDS layout: row r of a tile is 128 contiguous bytes = eight 16-byte
-// chunks; chunk c is stored in slot c ^ ((r >> 1) & 7).  A direct-to-LDS
+// chunks; chunk c is stored in slot c ^ ((r >> 1) & 7) (rows of 256 bytes
+// or more: c ^ (r & 15)).  A direct-to-LDS
 // load writes 64 lanes x 16 bytes contiguously, so each lane fetches the
 // global chunk that belongs in its slot.  With 64 four-byte banks, a
 // 16-byte read by 16 lanes of 16 consecutive rows at one k touches every
