@@ -6,6 +6,8 @@ gates of both widths, blocks without rotary, and mixtures of 2-64 experts
 with and without a shared expert.  Each configuration is checked as the
 fixed edge tests check theirs: float32 end to end against the fp64
 oracle, bf16 stage by stage from the GPU's own taps, routing exactly."""
+import os
+
 import numpy as np
 import pytest
 
@@ -44,8 +46,14 @@ def random_workload(i, dtype, rng):
     return synth.Workload(**w)
 
 
-def sweep(dtype, n=20):
-    rng = np.random.default_rng(20261202 if dtype == "f32" else 20261203)
+# RANDOM_SWEEP_N / RANDOM_SWEEP_SEED widen the sweep for a longer search
+# (the defaults are what the suite runs)
+SWEEP_N = int(os.environ.get("RANDOM_SWEEP_N", "20"))
+SWEEP_SEED = int(os.environ.get("RANDOM_SWEEP_SEED", "20261202"))
+
+
+def sweep(dtype, n=SWEEP_N):
+    rng = np.random.default_rng(SWEEP_SEED if dtype == "f32" else SWEEP_SEED + 1)
     return [random_workload(i, dtype, rng) for i in range(n)]
 
 
@@ -93,8 +101,8 @@ def random_large(i, rng):
     return synth.Workload(**w)
 
 
-_rng = np.random.default_rng(20261204)
-LARGE = [random_large(i, _rng) for i in range(8)]
+_rng = np.random.default_rng(SWEEP_SEED + 2)
+LARGE = [random_large(i, _rng) for i in range(int(os.environ.get("RANDOM_SWEEP_LARGE_N", "8")))]
 
 
 @pytest.mark.parametrize("w", LARGE, ids=lambda w: w.name)
