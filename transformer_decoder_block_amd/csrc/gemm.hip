@@ -1589,6 +1589,34 @@ static int cu_count() {
   return n;
 }
 
+// 256 x 128 tiles (8 waves of 64 x 64, the wave width of the staged
+// epilogues) for the last round of a persistent launch.
+using TileH = Tile<bf16, 256, 128, 4, 2, 128, 2>;
+
+// The same product restricted to output columns [n0, N): the first nb B
+// segments (those that hold output columns) start n0 rows later, and every
+// output and the residual start n0 columns later.
+template <typename T>
+static GemmParams column_window(const GemmParams& p, int n0, int nb) {
+  GemmParams q = p;
+  q.N = p.N - n0;
+  const int64_t skip = (int64_t)n0 * p.ldb;
+  for (int s = 0; s < nb; ++s) {
+    q.B[s] = (const T*)p.B[s] + skip;
+    q.b_bytes[s] = p.b_bytes[s] - (uint32_t)(skip * (int64_t)sizeof(T));
+    q.seg_end[s] = p.seg_end[s] - n0;
+  }
+  if (p.out)
+    q.out = p.out_f32 ? (void*)((float*)p.out + n0) : (void*)((T*)p.out + n0);
+  if (p.out_f32p) q.out_f32p = p.out_f32p + n0;
+  if (p.out_model) q.out_model = (T*)p.out_model + n0;
+  if (p.out_raw) q.out_raw = p.out_raw + n0;
+  if (p.resid)
+    q.resid = p.resid_f32 ? (const void*)((const float*)p.resid + n0)
+                          : (const void*)((const T*)p.resid + n0);
+  return q;
+}
+
 template <typename T, class TL, int EPI, bool GROUPED, int HDQ = 0>
 static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   const int n_per_tile = (EPI == EPI_SWIGLU) ? TL::BN / 2 : TL::BN;
@@ -1642,8 +1670,28 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
   }
   if constexpr (PERSIST && !GROUPED) {
     if (p.split_tiles == 0) {
+      const int cus = cu_count();
+      const int rem = tiles % cus;
+      const int c = rem / num_m;  // whole tile columns in the last round
+      if (tiles > cus && rem > 0 && rem <= cus / 2 && rem % num_m == 0 &&
+          p.nseg == (EPI == EPI_SWIGLU ? 2 : 1)) {
+        // The last round would leave half the CUs idle or more.  Its tiles
+        // are the last c tile columns: run them as twice as many 256 x 128
+        // tiles in a launch of their own, so every CU has one.
+        const int n0 = (num_n - c) * n_per_tile;
+        GemmParams head = p;
+        head.N = n0;
+        hipLaunchKernelGGL((gemm_persistent_kernel<T, TL, EPI, GROUPED>),
+                           dim3(std::min(tiles - rem, cus)), dim3(TL::NT), 0, s, head);
+        const GemmParams tail = column_window<T>(p, n0, EPI == EPI_SWIGLU ? 2 : 1);
+        const int tn = (EPI == EPI_SWIGLU) ? TileH::BN / 2 : TileH::BN;
+        hipLaunchKernelGGL((gemm_kernel<T, TileH, EPI, GROUPED>),
+                           dim3(num_m * ((tail.N + tn - 1) / tn)), dim3(TileH::NT), 0, s,
+                           tail);
+        return hipGetLastError();
+      }
       hipLaunchKernelGGL((gemm_persistent_kernel<T, TL, EPI, GROUPED>),
-                         dim3(std::min(tiles, cu_count())), dim3(TL::NT), 0, s, p);
+                         dim3(std::min(tiles, cus)), dim3(TL::NT), 0, s, p);
       return hipGetLastError();
     }
   }
