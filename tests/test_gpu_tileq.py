@@ -20,7 +20,9 @@ and 64, with hidden 256 so that the fp64 oracle evaluates every token:
   * stage C (layer_mid) on every row of every sequence, from the GPU's own
     q, k, v taps (head gate, o_proj, residual) and from its normed stream.
 
-The cases cover a ragged last M tile, sequences that start inside a tile,
+Where the grid's last round would fill at most half of the CUs, that round
+runs as 256 x 128 tiles (8 waves of 32 x 128) in a launch of its own; two
+cases reach it.  The cases cover a ragged last M tile, sequences that start inside a tile,
 sequence lengths that are not multiples of the 8- and 16-key groups of the
 transposed value store, the head-gate columns in a partial last N tile, a
 window, and GQA groups of 2, 4 and 6.
@@ -52,12 +54,21 @@ CASES = [
     # first starts inside an M tile and inside a 16-key group
     case("tileq_hd64_gate", 4, 1025, 32, 16, 64, qk_norm=True, sandwich=True,
          head_gate=32, window=300),
-    # 16 x 18 tiles, q/k norm with the query gain scaled 16x (sharp
+    # 16 x 18 tiles (the last two columns as 256 x 128 tiles), q/k norm
+    # with the query gain scaled 16x (sharp
     # attention); S % 8 = 5, so 8-key groups straddle two sequences
     case("tileq_hd128_g4_sharp", 3, 1365, 24, 6, 128, sharp=16, qk_norm=True,
          mlp="xielu"),
     # 16 x 16 tiles, hd 64, GQA 6, wq scaled 128x (sharp attention)
     case("tileq_hd64_g6_sharp", 4, 1024, 48, 8, 64, sharp=128),
+    # 16 x 20 tiles: the last round (64 tiles, the last four columns) runs
+    # as 256 x 128 tiles, which hold the k heads (q/k norm, rotary) and the
+    # v heads
+    case("tileq_tail_hd128", 4, 1024, 32, 4, 128, qk_norm=True),
+    # 16 x 21 tiles, the last five columns as 256 x 128 tiles: k, v and the
+    # head-gate columns, a ragged last M tile, S % 16 = 1 (V^T stores that
+    # straddle sequences), a window
+    case("tileq_tail_hd64_gate", 2, 2001, 64, 8, 64, head_gate=64, window=500),
 ]
 
 

@@ -1029,7 +1029,8 @@ gemm_kernel(const GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
   const int n_per_tile = PAIRED ? BN / 2 : BN;
-  const int num_n = (p.N + n_per_tile - 1) / n_per_tile;
+  const int nb0 = (EPI == EPI_QKV) ? p.n_base : 0;  // first output column
+  const int num_n = (p.N - nb0 + n_per_tile - 1) / n_per_tile;
 
   // ---- which tile
   int mt, nt, row_begin = 0, row_count = p.M, group = 0;
@@ -1140,10 +1141,10 @@ gemm_kernel(const GemmParams p) {
       n = nt * (BN / 2) + (lbase / WN) * half + (lrow % WN) % half;
       ok = n < p.N;
     } else {
-      const int nb = nt * BN + lbase;
+      const int nb = nb0 + nt * BN + lbase;
       seg = 0;
       while (seg < p.nseg - 1 && nb >= p.seg_end[seg]) ++seg;
-      n = nt * BN + lrow;
+      n = nb0 + nt * BN + lrow;
       ok = n < p.N;
       n -= seg ? p.seg_end[seg - 1] : 0;
     }
@@ -1250,7 +1251,7 @@ gemm_kernel(const GemmParams p) {
     // each wave stages its heads in its own slice of the (now idle) LDS
     const int lrow0 = mt * BM + wm * WM;
     T* slice = smem + wave * SLICE;
-    qkv_epilogue<T, HDQ, WM, WN>(acc, p, lrow0, nt * BN + wn * WN, lane, slice);
+    qkv_epilogue<T, HDQ, WM, WN>(acc, p, lrow0, nb0 + nt * BN + wn * WN, lane, slice);
     return;
   } else {
     tile_epilogue<T, TL, EPI>(p, acc, mt, nt, row_begin, row_count, wm, wn, lane);
@@ -1592,6 +1593,8 @@ static int cu_count() {
 // 256 x 128 tiles (8 waves of 64 x 64, the wave width of the staged
 // epilogues) for the last round of a persistent launch.
 using TileH = Tile<bf16, 256, 128, 4, 2, 128, 2>;
+// the q/k/v form: 8 waves of 32 x 128, whole heads per wave
+using TileQH = Tile<bf16, 256, 128, 8, 1, 128, 2>;
 
 // The same product restricted to output columns [n0, N): the first nb B
 // segments (those that hold output columns) start n0 rows later, and every
@@ -1692,6 +1695,24 @@ static hipError_t launch(const GemmParams& p0, int max_rows, hipStream_t s) {
       }
       hipLaunchKernelGGL((gemm_persistent_kernel<T, TL, EPI, GROUPED>),
                          dim3(std::min(tiles, cus)), dim3(TL::NT), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (EPI == EPI_QKV && TL::BM == 256 && TL::BN == 256) {
+    const int cus = cu_count();
+    const int rem = tiles % cus;
+    if (tiles > cus && rem > 0 && rem <= cus / 2 && rem % num_m == 0) {
+      // the last round as 256 x 128 tiles of the same heads, one per CU
+      const int n0 = (num_n - rem / num_m) * TL::BN;
+      GemmParams head = p;
+      head.N = n0;
+      hipLaunchKernelGGL((gemm_kernel<T, TL, EPI, GROUPED, HDQ>), dim3(tiles - rem),
+                         dim3(TL::NT), 0, s, head);
+      GemmParams tail = p;
+      tail.n_base = n0;
+      hipLaunchKernelGGL((gemm_kernel<T, TileQH, EPI, GROUPED, HDQ>),
+                         dim3(num_m * ((p.N - n0 + TileQH::BN - 1) / TileQH::BN)),
+                         dim3(TileQH::NT), 0, s, tail);
       return hipGetLastError();
     }
   }

@@ -88,6 +88,10 @@ struct GemmParams {
   size_t split_ws_bytes;
   int split_tiles;
   int split_parts;
+  // EPI_QKV only (set by gemm() for the last round of a large grid): the
+  // grid covers output columns [n_base, N); column indices stay global, so
+  // the segments and heads are found as for the whole product
+  int n_base;
 };
 
 hipError_t gemm(DType dt, EpiKind epi, const GemmParams& p, int max_rows,
